@@ -1,0 +1,158 @@
+/*
+ * pgemm.h -- persistent-tile-scheduled GEMM for AMD Instinct MI355X (gfx950).
+ *
+ * C-ABI boundary of the library: plain pointers and sizes, no C++ or torch
+ * types. All matrix pointers are DEVICE pointers (hipMalloc'd or torch
+ * tensors' data_ptr()); everything else is host memory.
+ *
+ * The operation (persistent-kernel forum thread, question): the GEMM
+ *     C[i][j] = sum_k A[i][k] * B[k][j]
+ * with A: M x K row-major (leading dimension K), B: K x N row-major
+ * (leading dimension N), C: M x N row-major (leading dimension N), all
+ * contiguous, accumulated in fp32. The output is cut into macro tiles and
+ * a tile scheduler hands tiles to workgroups (same question). Scheduling
+ * never changes the value of C: every mode runs the same tile body, so C is
+ * bitwise identical across modes and reruns (KernelWiki "Persistent
+ * Kernels with Cluster Launch Control", "Choosing between static and CLC
+ * scheduling": neither scheduler adds work).
+ *
+ * Errors: every entry point returns a pgemm_status_t. No C++ exception
+ * crosses this boundary. Launches are asynchronous on the handle's stream;
+ * errors of the launch itself are returned as PGEMM_ERR_HIP, with detail
+ * in pgemm_last_error(). A handle is not thread-safe: use one handle per
+ * stream used concurrently (the dynamic scheduler's work counter is per
+ * handle).
+ */
+#ifndef PGEMM_H
+#define PGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct pgemm_ctx* pgemm_handle_t;
+
+typedef enum {
+  PGEMM_OK = 0,
+  PGEMM_ERR_INVALID_ARG = 1, /* null pointer with non-zero size, negative size, bad enum */
+  PGEMM_ERR_UNSUPPORTED = 2, /* size beyond the 32-bit tile/offset limits */
+  PGEMM_ERR_HIP = 3,         /* a HIP runtime call failed; see pgemm_last_error() */
+  PGEMM_ERR_OOM = 4          /* device or host allocation failed */
+} pgemm_status_t;
+
+/* Element formats. The pages name fp16 and fp8 (Triton persistent-matmul
+ * issue: "--prec fp16", and the fp8 example on H100); bf16 is the other
+ * 16-bit format of the same MFMA family. fp8 is OCP E4M3 ("fn": bias 7,
+ * max 448, no infinities) with a per-tensor scale of 1.0. */
+typedef enum {
+  PGEMM_F16 = 0,         /* A, B, C: IEEE binary16 */
+  PGEMM_BF16 = 1,        /* A, B, C: bfloat16 */
+  PGEMM_F8E4M3_BF16 = 2  /* A, B: OCP e4m3 (1 byte); C: bfloat16 */
+} pgemm_dtype_t;
+
+/* Tile scheduling modes.
+ * NONPERSISTENT: one workgroup per output tile (forum thread, question:
+ *   "a thread block for each tile"); grid = number of tiles T.
+ * STATIC: a persistent grid of G workgroups (forum thread, question: block
+ *   count set to the SM count; first answer: sized so all blocks stay
+ *   resident); workgroup w computes tiles w, w+G, w+2G, ... of the tile
+ *   order, a deterministic mapping (KernelWiki, "Choosing between static
+ *   and CLC scheduling").
+ * DYNAMIC: a persistent grid of G workgroups; workgroup w starts on tile
+ *   w, then claims further tile ids from a device-wide atomic work counter
+ *   until a claim fails, after which it never claims again -- the AMD
+ *   analogue of cluster launch control's cancel-and-reuse (KernelWiki,
+ *   intro), not a port of it. */
+typedef enum {
+  PGEMM_SCHED_NONPERSISTENT = 0,
+  PGEMM_SCHED_STATIC = 1,
+  PGEMM_SCHED_DYNAMIC = 2
+} pgemm_sched_t;
+
+/* Create a handle on HIP device `device` (which becomes current). Allocates
+ * the dynamic scheduler's device work counter (zeroed) and caches the CU
+ * count. The handle starts on the null stream. *out is NULL on failure. */
+int pgemm_create(pgemm_handle_t* out, int device);
+
+/* Bind a hipStream_t (passed as void*; NULL = null stream). Later runs
+ * enqueue on it. */
+int pgemm_set_stream(pgemm_handle_t h, void* hip_stream);
+
+/* Enqueue C = A * B on the handle's stream; returns without waiting.
+ *   A, B, C: device pointers to contiguous row-major matrices (layouts
+ *     above); they must not alias and must stay valid until the work is
+ *     done. The caller owns them.
+ *   M, N, K: sizes, each in [0, 2^31 - 1]. M == 0 or N == 0: no work, OK.
+ *     K == 0: C is filled with zeros (an empty sum).
+ *   dtype: pgemm_dtype_t.
+ *   sched_mode: pgemm_sched_t.
+ *   grid_multiple: persistent modes only (ignored for NONPERSISTENT).
+ *     <= 0: G = occupancy x CU count (all workgroups co-resident, the
+ *     sizing of the forum thread's first answer); > 0: G = grid_multiple x
+ *     CU count (the NUM_SMS multiple of the Triton issue's follow-up
+ *     comment), which may exceed co-residency -- no workgroup waits on
+ *     another, so that stays correct. G is clamped to the tile count T.
+ * Operands whose K and N are multiples of 16 bytes of elements (8 for
+ * fp16/bf16, 16 for fp8) with 16-byte-aligned A, B and 8-byte-aligned C
+ * take the fast 256 x 256 tile kernel; others take a generic 64 x 64 tile
+ * kernel with the same schedulers (correct, slower). */
+int pgemm_run(pgemm_handle_t h, const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+              int dtype, int sched_mode, int grid_multiple);
+
+/* Wait for the handle's stream, free the work counter and the handle.
+ * NULL is accepted (no-op). */
+int pgemm_destroy(pgemm_handle_t h);
+
+/* Static text for a status code. */
+const char* pgemm_status_string(int status);
+
+/* Detail of the last failure on this handle ("" if none). Valid until the
+ * next call on the handle. */
+const char* pgemm_last_error(pgemm_handle_t h);
+
+/* ---- checking and reporting (not for timed runs) ---------------------- */
+
+/* Attach a caller-owned device int32 array of n_tiles entries. Each run
+ * then atomically adds 1 to visits[t] after tile t's C store, so after a
+ * run from zeroed memory every entry must read exactly 1 (every tile
+ * written exactly once). dev_visits == NULL detaches. Runs whose tile
+ * count exceeds n_tiles fail with PGEMM_ERR_INVALID_ARG. */
+int pgemm_set_tile_counter(pgemm_handle_t h, int32_t* dev_visits, int64_t n_tiles);
+
+/* Attach a caller-owned device int32 array of n_tiles entries; each run
+ * writes owner[t] = the id of the workgroup that computed tile t. NULL
+ * detaches. Same size rule as the visit counter. */
+int pgemm_set_owner_log(pgemm_handle_t h, int32_t* dev_owner, int64_t n_tiles);
+
+/* Report how pgemm_run would launch this problem, without launching:
+ * tile count, grid size, occupancy (workgroups per CU), macro tile
+ * (bm x bn, k-step bk in elements), and whether the fast kernel is used.
+ * Output pointers may be NULL. Alignment is judged from the sizes only
+ * (pointers assumed 16-byte aligned). */
+int pgemm_query_launch(pgemm_handle_t h, int64_t M, int64_t N, int64_t K, int dtype, int sched_mode,
+                       int grid_multiple, int* tiles, int* grid, int* occupancy, int* bm, int* bn, int* bk,
+                       int* fast_path);
+
+/* Tile-order knobs: GROUP_SIZE_M of the grouped order (default 8, the
+ * Triton issue's setting; 1 = row-major), and the XCD-aware remap (1 = on,
+ * the default; 0 = off). Both apply identically to all modes. */
+int pgemm_set_tile_order(pgemm_handle_t h, int group_m, int xcd_remap);
+
+/* Host mirror of the device tile order: (pid_m, pid_n) of tile t for an
+ * n_m x n_n tile grid, with the same knobs and CU-count chunking the
+ * device uses (cu_chunk = CU count, or 0 for no XCD remap). Pure function,
+ * no GPU needed. */
+int pgemm_tile_coords(int64_t t, int64_t n_m, int64_t n_n, int group_m, int cu_chunk, int* pid_m,
+                      int* pid_n);
+
+/* Read the device work counter (synchronizes the handle's stream). It
+ * reads 0 between launches; any other value means a launch was cut short. */
+int pgemm_read_work_counter(pgemm_handle_t h, int32_t* value);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PGEMM_H */

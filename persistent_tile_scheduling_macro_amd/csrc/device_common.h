@@ -1,0 +1,193 @@
+// Device-side building blocks shared by the GEMM kernels: element traits,
+// fragment types, buffer resources and zero-filling LDS loads, the tile
+// order, and the three tile schedulers.
+//
+// The operation is the GEMM of the persistent-kernel forum thread
+// (question): C = A*B cut into output tiles, each tile handed to one
+// workgroup by a tile scheduler. Layouts: A is M x K row-major, B is K x N
+// row-major, C is M x N row-major.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace pgemm {
+
+// ---------------------------------------------------------------- types
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef int intx8_t __attribute__((ext_vector_type(8)));
+typedef int intx4_t __attribute__((ext_vector_type(4)));
+typedef int intx2_t __attribute__((ext_vector_type(2)));
+typedef __fp16 fp16x4_raw_t __attribute__((__vector_size__(8)));
+
+#define PGEMM_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+enum DType : int { kF16 = 0, kBF16 = 1, kF8E4M3 = 2 };
+enum Sched : int { kNonPersistent = 0, kStatic = 1, kDynamic = 2 };
+
+// Per-dtype facts used by the kernels. A "k-group" is the reduction depth
+// of one MFMA: 32 for the 16-bit types (v_mfma_f32_16x16x32_{f16,bf16}),
+// 128 for OCP e4m3 (v_mfma_f32_16x16x128_f8f6f4). Each lane of a 16x16
+// MFMA holds 16 bytes (16-bit types) or 32 bytes (fp8) of one row of A and
+// of one column of B.
+template <int DT> struct Traits;
+template <> struct Traits<kF16> {
+  static constexpr int esize = 2;   // bytes per input element
+  static constexpr int kgroup = 32; // k per MFMA
+  typedef _Float16 out_t;
+};
+template <> struct Traits<kBF16> {
+  static constexpr int esize = 2;
+  static constexpr int kgroup = 32;
+  typedef __bf16 out_t;
+};
+template <> struct Traits<kF8E4M3> {
+  static constexpr int esize = 1;
+  static constexpr int kgroup = 128;
+  typedef __bf16 out_t;
+};
+
+// ------------------------------------------------------- kernel arguments
+struct Params {
+  const uint8_t* A;
+  const uint8_t* B;
+  uint8_t* C;
+  int M, N, K;
+  int n_m, n_n, T; // tile grid and tile count
+  int G;           // workgroups launched
+  int group_m;     // GROUP_SIZE_M of the tile order (>= 1)
+  int xcd_chunk;   // >0: XCD-aware remap inside chunks of this many tiles
+  int* counter;    // dynamic scheduler's work counter (reads 0 between launches)
+  int* visits;     // optional int32[T] tile-visit counter
+  int* owner;      // optional int32[T] owner log (workgroup id per tile)
+};
+
+// ------------------------------------------------------------ tile order
+// Tile id t -> (pid_m, pid_n). Two steps, applied identically in every
+// scheduling mode so that only the scheduling differs between modes:
+//
+// 1. XCD-aware remap. Workgroup ids are dispatched round-robin over the 8
+//    XCDs, and in the persistent modes workgroup w owns tiles t = w (mod G)
+//    with G a multiple of the CU count, so t mod 8 names the XCD that runs
+//    t. Inside each full chunk of `xcd_chunk` tiles the remap makes each
+//    XCD's tiles consecutive, so step 2 gives every XCD a compact block of
+//    the output (shared operand rows and columns stay in that XCD's L2).
+// 2. Grouped order (the GROUP_SIZE_M knob of the Triton persistent-matmul
+//    issue, "What I've tried" / follow-up comment): walk down groups of
+//    group_m tile rows column by column. group_m = 1 is plain row-major.
+__host__ __device__ inline int xcd_remap(int t, int T, int chunk) {
+  if (chunk <= 0 || (chunk & 7) != 0) return t;
+  int base = t - t % chunk;
+  if (base + chunk > T) return t; // partial last chunk keeps the identity order
+  int u = t - base;
+  return base + (u & 7) * (chunk >> 3) + (u >> 3);
+}
+
+__host__ __device__ inline void grouped_tile(int t, int n_m, int n_n, int group_m, int* pm, int* pn) {
+  int width = group_m * n_n;
+  int group = t / width;
+  int first_m = group * group_m;
+  int gs = n_m - first_m < group_m ? n_m - first_m : group_m;
+  int r = t - group * width;
+  *pm = first_m + r % gs;
+  *pn = r / gs;
+}
+
+__host__ __device__ inline void tile_coords(int t, const Params& p, int* pm, int* pn) {
+  grouped_tile(xcd_remap(t, p.T, p.xcd_chunk), p.n_m, p.n_n, p.group_m, pm, pn);
+}
+
+// ---------------------------------------------------- dynamic work counter
+// Claim protocol of the dynamic persistent mode. It is the AMD analogue of
+// cluster launch control (KernelWiki "Persistent Kernels with Cluster Launch
+// Control", intro): the grid defines the candidate ids, a claim returns the
+// next unstarted id, and a failed claim means the worker never claims again.
+// Every workgroup starts on tile blockIdx.x without a claim; each further
+// claim returns counter+G. Each workgroup makes exactly one failing claim,
+// so one launch makes exactly T claims, returning the counter values
+// 0..T-1 once each; the claim that returns T-1 is the last one and resets
+// the counter to 0 for the next launch on the stream.
+// A counter value outside [0, T) cannot come from this protocol; it is
+// treated as a failed claim so a corrupted counter can never index a tile
+// outside the grid.
+__device__ inline int claim_tile(int* counter, int T, int G) {
+  int c = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (c == T - 1) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return (c < 0 || c >= T) ? T : c + G;
+}
+
+// ------------------------------------------------ buffer loads into LDS
+// gfx9 buffer resource word 3 for raw (untyped) dword access.
+constexpr int kRsrcWord3 = 0x00020000;
+// Any lane offset >= num_records reads zeros; masked lanes use this offset.
+constexpr uint32_t kOOB = 0x80000000u;
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF, kRsrcWord3);
+}
+
+// One wave-wide 16-byte-per-lane load straight into LDS: lane l's 16 bytes
+// land at lds + 16*l (a contiguous 1 KiB per wave). Offsets >= 2^31 read 0.
+__device__ inline void load16_to_lds(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, PGEMM_LDS(void, lds), 16, voffset, 0, 0, 0);
+}
+
+// --------------------------------------------------------------- MFMA
+// 16x16 output block; lane l holds rows 4*(l/16)+r, column l%16 of D, r<4.
+// Both operands: lane l holds row (or column) l%16 and the k-slots of group
+// l/16; the pairing of A and B k-slots is positional, so any k order that
+// both operands share gives the same sum.
+__device__ inline floatx4_t mfma(const half8_t& a, const half8_t& b, floatx4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ inline floatx4_t mfma(const bf16x8_t& a, const bf16x8_t& b, floatx4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ inline floatx4_t mfma(const intx8_t& a, const intx8_t& b, floatx4_t c) {
+  // format codes 0/0: both operands OCP fp8 e4m3; zero scale operands select
+  // the unscaled instruction (per-tensor scale 1.0)
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// The same MFMAs with the accumulator pinned to AGPRs and tied (dst ==
+// srcC). Used for the 256-register accumulator tile of the fast kernel,
+// where the compiler otherwise renames accumulators between the two
+// register files on every MFMA. Not volatile, so LDS reads and buffer loads
+// still schedule around them. Callers must leave >= 24 wait states between
+// the last MFMA and any read of the accumulators (see acc_drain()).
+__device__ inline void mfma_acc(floatx4_t& c, const half8_t& a, const half8_t& b) {
+  asm("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+__device__ inline void mfma_acc(floatx4_t& c, const bf16x8_t& a, const bf16x8_t& b) {
+  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+__device__ inline void mfma_acc(floatx4_t& c, const intx8_t& a, const intx8_t& b) {
+  asm("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+// Wait states between MFMAs issued as inline asm and a VALU / accvgpr read
+// of their results (the compiler cannot see the asm's latency).
+__device__ inline void acc_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+
+// --------------------------------------------------------- output rounding
+// fp32 -> fp16 / bf16, IEEE round to nearest even.
+__device__ inline _Float16 to_out(float x, _Float16*) { return (_Float16)x; }
+__device__ inline __bf16 to_out(float x, __bf16*) { return (__bf16)x; }
+
+template <class OutT>
+__device__ inline void store4(OutT* dst, floatx4_t v) {
+  typedef OutT v4 __attribute__((ext_vector_type(4)));
+  v4 o;
+  o[0] = to_out(v[0], (OutT*)nullptr);
+  o[1] = to_out(v[1], (OutT*)nullptr);
+  o[2] = to_out(v[2], (OutT*)nullptr);
+  o[3] = to_out(v[3], (OutT*)nullptr);
+  *reinterpret_cast<v4*>(dst) = o;
+}
+
+} // namespace pgemm

@@ -1,0 +1,291 @@
+// Host side of the library: argument validation, kernel selection, grid
+// sizing, the work counter, and the C-ABI entry points declared in
+// include/pgemm.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+
+#include "../../include/pgemm.h"
+#include "kernels.h"
+
+using namespace pgemm;
+
+struct pgemm_ctx {
+  int device = 0;
+  hipStream_t stream = nullptr;
+  int cus = 0;
+  int* counter = nullptr; // dynamic scheduler's work counter (device int32)
+  int32_t* visits = nullptr;
+  int64_t n_visits = 0;
+  int32_t* owner = nullptr;
+  int64_t n_owner = 0;
+  int group_m = 8;
+  int xcd_remap = 1;
+  char last_error[512] = {0};
+};
+
+namespace {
+
+int fail(pgemm_ctx* h, int status, const char* fmt, ...) {
+  if (h) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(h->last_error, sizeof(h->last_error), fmt, ap);
+    va_end(ap);
+  }
+  return status;
+}
+
+// Macro-tile facts of the two kernel bodies (the kernels themselves live in
+// the per-dtype translation units).
+constexpr int kFastBM = 256, kFastBN = 256, kFastThreads = 256;
+constexpr int kGenBM = 64, kGenBN = 64, kGenThreads = 256;
+int fast_block_k(int dtype) { return dtype == kF8E4M3 ? 128 : 64; }
+
+kernel_fn pick_kernel(int dtype, int sched, bool fast_path) {
+  switch (dtype) {
+    case kF16: return pick_kernel_f16(sched, fast_path);
+    case kBF16: return pick_kernel_bf16(sched, fast_path);
+    default: return pick_kernel_f8(sched, fast_path);
+  }
+}
+
+int esize_of(int dtype) { return dtype == kF8E4M3 ? 1 : 2; }
+
+bool sizes_fast(int dtype, int64_t N, int64_t K) {
+  const int per16 = 16 / esize_of(dtype); // elements per 16 bytes
+  return (K % per16) == 0 && (N % per16) == 0;
+}
+
+bool ptrs_fast(const void* A, const void* B, const void* C) {
+  return ((uintptr_t)A % 16) == 0 && ((uintptr_t)B % 16) == 0 && ((uintptr_t)C % 8) == 0;
+}
+
+struct Plan {
+  bool fast;
+  int bm, bn, bk;
+  int64_t n_m, n_n, T;
+  int occupancy;
+  int64_t G;
+};
+
+int plan_launch(pgemm_ctx* h, int64_t M, int64_t N, int64_t K, int dtype, int sched, int grid_multiple,
+                bool fast, Plan* pl) {
+  pl->fast = fast;
+  pl->bm = fast ? kFastBM : kGenBM;
+  pl->bn = fast ? kFastBN : kGenBN;
+  pl->bk = fast ? fast_block_k(dtype) : (dtype == kF8E4M3 ? 128 : 32);
+  pl->n_m = (M + pl->bm - 1) / pl->bm;
+  pl->n_n = (N + pl->bn - 1) / pl->bn;
+  pl->T = pl->n_m * pl->n_n;
+  // tile ids and claims (< T + G <= 2T) stay inside int32
+  if (pl->T >= ((int64_t)1 << 30))
+    return fail(h, PGEMM_ERR_UNSUPPORTED, "tile count %lld exceeds 2^30-1", (long long)pl->T);
+  if (fast) {
+    // per-tile A offsets reach 256 rows of K elements; per-step B offsets reach BK rows of N
+    const int64_t es = esize_of(dtype);
+    if ((int64_t)kFastBM * K * es >= ((int64_t)1 << 31) || (int64_t)pl->bk * N * es >= ((int64_t)1 << 31))
+      return fail(h, PGEMM_ERR_UNSUPPORTED, "operand rows too long for 32-bit buffer offsets");
+  }
+  kernel_fn k = pick_kernel(dtype, sched, fast);
+  int occ = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(k),
+                                                              fast ? kFastThreads : kGenThreads, 0);
+  if (e != hipSuccess) return fail(h, PGEMM_ERR_HIP, "occupancy query: %s", hipGetErrorString(e));
+  if (occ < 1) occ = 1;
+  pl->occupancy = occ;
+  if (sched == kNonPersistent) {
+    pl->G = pl->T;
+  } else {
+    const int64_t mult = grid_multiple <= 0 ? occ : grid_multiple;
+    pl->G = std::min<int64_t>(mult * h->cus, pl->T);
+  }
+  return PGEMM_OK;
+}
+
+int check_common(pgemm_ctx* h, int64_t M, int64_t N, int64_t K, int dtype, int sched) {
+  if (!h) return PGEMM_ERR_INVALID_ARG;
+  if (M < 0 || N < 0 || K < 0)
+    return fail(h, PGEMM_ERR_INVALID_ARG, "negative size M=%lld N=%lld K=%lld", (long long)M, (long long)N,
+                (long long)K);
+  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX)
+    return fail(h, PGEMM_ERR_UNSUPPORTED, "sizes must be below 2^31");
+  if (dtype < PGEMM_F16 || dtype > PGEMM_F8E4M3_BF16) return fail(h, PGEMM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (sched < PGEMM_SCHED_NONPERSISTENT || sched > PGEMM_SCHED_DYNAMIC)
+    return fail(h, PGEMM_ERR_INVALID_ARG, "unknown sched_mode %d", sched);
+  return PGEMM_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+int pgemm_create(pgemm_handle_t* out, int device) {
+  if (!out) return PGEMM_ERR_INVALID_ARG;
+  *out = nullptr;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || device < 0 || device >= ndev) return PGEMM_ERR_INVALID_ARG;
+  pgemm_ctx* h = new (std::nothrow) pgemm_ctx();
+  if (!h) return PGEMM_ERR_OOM;
+  h->device = device;
+  if (hipSetDevice(device) != hipSuccess || hipDeviceGetAttribute(&h->cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) {
+    delete h;
+    return PGEMM_ERR_HIP;
+  }
+  // The counter gets a 256-byte allocation of its own so no other data shares its cache line.
+  if (hipMalloc(&h->counter, 256) != hipSuccess) {
+    delete h;
+    return PGEMM_ERR_OOM;
+  }
+  if (hipMemset(h->counter, 0, 256) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    hipFree(h->counter);
+    delete h;
+    return PGEMM_ERR_HIP;
+  }
+  if (const char* g = getenv("PGEMM_GROUP_M")) h->group_m = std::max(1, atoi(g));
+  if (const char* x = getenv("PGEMM_XCD_REMAP")) h->xcd_remap = atoi(x) != 0;
+  *out = h;
+  return PGEMM_OK;
+}
+
+int pgemm_set_stream(pgemm_handle_t h, void* hip_stream) {
+  if (!h) return PGEMM_ERR_INVALID_ARG;
+  h->stream = reinterpret_cast<hipStream_t>(hip_stream);
+  return PGEMM_OK;
+}
+
+int pgemm_run(pgemm_handle_t h, const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+              int dtype, int sched_mode, int grid_multiple) {
+  int rc = check_common(h, M, N, K, dtype, sched_mode);
+  if (rc != PGEMM_OK) return rc;
+  h->last_error[0] = 0;
+  if (M == 0 || N == 0) return PGEMM_OK;
+  if (!C) return fail(h, PGEMM_ERR_INVALID_ARG, "C is NULL");
+  if (hipSetDevice(h->device) != hipSuccess) return fail(h, PGEMM_ERR_HIP, "hipSetDevice failed");
+  if (K == 0) {
+    launch_fill_zero(C, M * N, h->stream);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? PGEMM_OK : fail(h, PGEMM_ERR_HIP, "zero-fill launch: %s", hipGetErrorString(e));
+  }
+  if (!A || !B) return fail(h, PGEMM_ERR_INVALID_ARG, "A or B is NULL");
+  const bool fast = sizes_fast(dtype, N, K) && ptrs_fast(A, B, C);
+  Plan pl;
+  rc = plan_launch(h, M, N, K, dtype, sched_mode, grid_multiple, fast, &pl);
+  if (rc != PGEMM_OK) return rc;
+  if (h->visits && pl.T > h->n_visits)
+    return fail(h, PGEMM_ERR_INVALID_ARG, "tile counter holds %lld entries, run has %lld tiles",
+                (long long)h->n_visits, (long long)pl.T);
+  if (h->owner && pl.T > h->n_owner)
+    return fail(h, PGEMM_ERR_INVALID_ARG, "owner log holds %lld entries, run has %lld tiles", (long long)h->n_owner,
+                (long long)pl.T);
+  Params p;
+  p.A = static_cast<const uint8_t*>(A);
+  p.B = static_cast<const uint8_t*>(B);
+  p.C = static_cast<uint8_t*>(C);
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.n_m = (int)pl.n_m;
+  p.n_n = (int)pl.n_n;
+  p.T = (int)pl.T;
+  p.G = (int)pl.G;
+  p.group_m = h->group_m;
+  p.xcd_chunk = h->xcd_remap ? h->cus : 0;
+  p.counter = h->counter;
+  p.visits = h->visits;
+  p.owner = h->owner;
+  kernel_fn k = pick_kernel(dtype, sched_mode, fast);
+  hipLaunchKernelGGL(k, dim3((unsigned)pl.G), dim3(fast ? kFastThreads : kGenThreads), 0, h->stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(h, PGEMM_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+  return PGEMM_OK;
+}
+
+int pgemm_destroy(pgemm_handle_t h) {
+  if (!h) return PGEMM_OK;
+  int rc = PGEMM_OK;
+  if (hipSetDevice(h->device) != hipSuccess) rc = PGEMM_ERR_HIP;
+  if (hipStreamSynchronize(h->stream) != hipSuccess) rc = PGEMM_ERR_HIP;
+  if (hipFree(h->counter) != hipSuccess) rc = PGEMM_ERR_HIP;
+  delete h;
+  return rc;
+}
+
+const char* pgemm_status_string(int status) {
+  switch (status) {
+    case PGEMM_OK: return "PGEMM_OK";
+    case PGEMM_ERR_INVALID_ARG: return "PGEMM_ERR_INVALID_ARG";
+    case PGEMM_ERR_UNSUPPORTED: return "PGEMM_ERR_UNSUPPORTED";
+    case PGEMM_ERR_HIP: return "PGEMM_ERR_HIP";
+    case PGEMM_ERR_OOM: return "PGEMM_ERR_OOM";
+    default: return "PGEMM_ERR_UNKNOWN";
+  }
+}
+
+const char* pgemm_last_error(pgemm_handle_t h) { return h ? h->last_error : "invalid handle"; }
+
+int pgemm_set_tile_counter(pgemm_handle_t h, int32_t* dev_visits, int64_t n_tiles) {
+  if (!h) return PGEMM_ERR_INVALID_ARG;
+  if (dev_visits && n_tiles <= 0) return fail(h, PGEMM_ERR_INVALID_ARG, "n_tiles must be positive");
+  h->visits = dev_visits;
+  h->n_visits = dev_visits ? n_tiles : 0;
+  return PGEMM_OK;
+}
+
+int pgemm_set_owner_log(pgemm_handle_t h, int32_t* dev_owner, int64_t n_tiles) {
+  if (!h) return PGEMM_ERR_INVALID_ARG;
+  if (dev_owner && n_tiles <= 0) return fail(h, PGEMM_ERR_INVALID_ARG, "n_tiles must be positive");
+  h->owner = dev_owner;
+  h->n_owner = dev_owner ? n_tiles : 0;
+  return PGEMM_OK;
+}
+
+int pgemm_query_launch(pgemm_handle_t h, int64_t M, int64_t N, int64_t K, int dtype, int sched_mode,
+                       int grid_multiple, int* tiles, int* grid, int* occupancy, int* bm, int* bn, int* bk,
+                       int* fast_path) {
+  int rc = check_common(h, M, N, K, dtype, sched_mode);
+  if (rc != PGEMM_OK) return rc;
+  Plan pl;
+  rc = plan_launch(h, M, N, K, dtype, sched_mode, grid_multiple, sizes_fast(dtype, N, K), &pl);
+  if (rc != PGEMM_OK) return rc;
+  if (tiles) *tiles = (int)pl.T;
+  if (grid) *grid = (int)pl.G;
+  if (occupancy) *occupancy = pl.occupancy;
+  if (bm) *bm = pl.bm;
+  if (bn) *bn = pl.bn;
+  if (bk) *bk = pl.bk;
+  if (fast_path) *fast_path = pl.fast ? 1 : 0;
+  return PGEMM_OK;
+}
+
+int pgemm_set_tile_order(pgemm_handle_t h, int group_m, int xcd_remap) {
+  if (!h) return PGEMM_ERR_INVALID_ARG;
+  if (group_m < 1) return fail(h, PGEMM_ERR_INVALID_ARG, "group_m must be >= 1");
+  h->group_m = group_m;
+  h->xcd_remap = xcd_remap != 0;
+  return PGEMM_OK;
+}
+
+int pgemm_tile_coords(int64_t t, int64_t n_m, int64_t n_n, int group_m, int cu_chunk, int* pid_m, int* pid_n) {
+  if (n_m <= 0 || n_n <= 0 || group_m < 1 || t < 0 || n_m * n_n >= ((int64_t)1 << 31) || t >= n_m * n_n || !pid_m ||
+      !pid_n)
+    return PGEMM_ERR_INVALID_ARG;
+  const int T = (int)(n_m * n_n);
+  grouped_tile(xcd_remap((int)t, T, cu_chunk), (int)n_m, (int)n_n, group_m, pid_m, pid_n);
+  return PGEMM_OK;
+}
+
+int pgemm_read_work_counter(pgemm_handle_t h, int32_t* value) {
+  if (!h || !value) return PGEMM_ERR_INVALID_ARG;
+  if (hipSetDevice(h->device) != hipSuccess) return fail(h, PGEMM_ERR_HIP, "hipSetDevice failed");
+  hipError_t e = hipMemcpyAsync(value, h->counter, sizeof(int32_t), hipMemcpyDeviceToHost, h->stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(h->stream);
+  return e == hipSuccess ? PGEMM_OK : fail(h, PGEMM_ERR_HIP, "counter read: %s", hipGetErrorString(e));
+}
+
+} // extern "C"

@@ -1,0 +1,88 @@
+"""CPU-side checks of the C-ABI library: it loads, exports every entry point
+that include/pgemm.h declares, and its host logic (status strings, argument
+checks that need no device, the tile order) behaves as documented."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pgemm.h")
+
+
+@pytest.fixture(scope="module")
+def pg():
+    import persistent_tile_scheduling_macro_amd as pg
+    return pg
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pgemm_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol(pg):
+    names = declared_functions()
+    assert len(names) >= 12, names
+    lib = ctypes.CDLL(pg.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(pg):
+    assert pg.pgemm_status_string(0) == "PGEMM_OK"
+    assert pg.pgemm_status_string(1) == "PGEMM_ERR_INVALID_ARG"
+    assert pg.pgemm_status_string(99) == "PGEMM_ERR_UNKNOWN"
+
+
+def test_null_handle_is_rejected(pg):
+    with pytest.raises(pg.PgemmError) as e:
+        pg.pgemm_run(None, 0, 0, 0, 1, 1, 1, 0, 0, 0)
+    assert e.value.status == pg.PGEMM_ERR_INVALID_ARG
+    assert pg.pgemm_last_error(None) == "invalid handle"
+    pg.pgemm_destroy(None)  # documented no-op
+
+
+def test_tile_order_row_major_when_group_is_one(pg):
+    for n_m, n_n in [(1, 1), (3, 5), (7, 2)]:
+        for t in range(n_m * n_n):
+            assert pg.pgemm_tile_coords(t, n_m, n_n, 1, 0) == (t // n_n, t % n_n)
+
+
+@pytest.mark.parametrize("n_m,n_n,g,chunk", [(32, 32, 8, 256), (33, 33, 8, 256), (24, 24, 8, 256),
+                                              (16, 64, 4, 256), (5, 7, 3, 0), (16, 16, 8, 256), (1, 9, 8, 8)])
+def test_tile_order_is_a_bijection(pg, n_m, n_n, g, chunk):
+    seen = set()
+    for t in range(n_m * n_n):
+        pm, pn = pg.pgemm_tile_coords(t, n_m, n_n, g, chunk)
+        assert 0 <= pm < n_m and 0 <= pn < n_n
+        seen.add((pm, pn))
+    assert len(seen) == n_m * n_n
+
+
+def test_grouped_order_walks_columns_inside_a_group(pg):
+    # group_m = 8 over a 16 x 4 grid, no XCD remap: tiles 0..7 are rows 0..7 of column 0,
+    # 8..15 rows 0..7 of column 1, ...; the second group starts at row 8.
+    assert [pg.pgemm_tile_coords(t, 16, 4, 8, 0) for t in range(9)] == \
+        [(r, 0) for r in range(8)] + [(0, 1)]
+    assert pg.pgemm_tile_coords(32, 16, 4, 8, 0) == (8, 0)
+
+
+def test_xcd_remap_gives_each_xcd_a_compact_block(pg):
+    # 32 x 32 tiles, chunks of 256 (the CU count): tile ids t = x (mod 8) run on XCD x;
+    # after the remap each XCD's 32 tiles in a chunk form an 8-row x 4-column block.
+    for chunk_start in (0, 256):
+        for x in range(8):
+            coords = [pg.pgemm_tile_coords(chunk_start + x + 8 * j, 32, 32, 8, 256) for j in range(32)]
+            rows = {pm for pm, _ in coords}
+            cols = {pn for _, pn in coords}
+            assert len(rows) == 8 and len(cols) == 4, (x, rows, cols)
+
+
+def test_tile_coords_rejects_bad_arguments(pg):
+    with pytest.raises(pg.PgemmError):
+        pg.pgemm_tile_coords(6, 2, 3, 1, 0)
+    with pytest.raises(pg.PgemmError):
+        pg.pgemm_tile_coords(0, 2, 3, 0, 0)

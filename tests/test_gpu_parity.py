@@ -1,0 +1,206 @@
+"""GPU parity: every scheduling mode x dtype against the CPU oracle, through the C ABI.
+
+Checks, per case (see the oracle's header for what is computed):
+* normwise error ||C - C_ref||_F / ||C_ref||_F <= 2e-3 (fp16/bf16 out) or
+  <= 1e-2 (fp8 in, bf16 out);
+* small-integer inputs: bit-exact against the oracle's value rounded to the
+  output type (every partial sum is an integer below 2^24, exact in fp32 in
+  any order);
+* tile-visit counter: every output tile written exactly once;
+* C bitwise identical across the three modes (one tile body).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import seeded_inputs as si
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f16": 0, "bf16": 1, "e4m3fn": 2}
+OUT = {"f16": ("f16", torch.float16), "bf16": ("bf16", torch.bfloat16), "e4m3fn": ("bf16", torch.bfloat16)}
+TOL = {"f16": 2e-3, "bf16": 2e-3, "e4m3fn": 1e-2}
+MODES = [0, 1, 2]
+
+
+@pytest.fixture(scope="module")
+def pg():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import persistent_tile_scheduling_macro_amd as pg
+    return pg
+
+
+@pytest.fixture(scope="module")
+def handle(pg):
+    h = pg.pgemm_create(0)
+    yield h
+    pg.pgemm_destroy(h)
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def run(pg, h, A, B, dtype, mode, grid_multiple=0, visits=True):
+    """Run C = A @ B on the GPU; returns (C bits, visits array or None, launch info)."""
+    M, K = A.shape
+    N = B.shape[1]
+    dev = torch.device("cuda:0")
+    Ad, Bd = A.to(dev), B.to(dev)
+    C = torch.full((M, N), float("nan"), dtype=OUT[dtype][1], device=dev)
+    info = pg.pgemm_query_launch(h, M, N, K, DT[dtype], mode, grid_multiple)
+    v = None
+    if visits and M and N and K:
+        v = torch.zeros(max(info["tiles"], 1), dtype=torch.int32, device=dev)
+        pg.pgemm_set_tile_counter(h, v)
+    try:
+        pg.pgemm_run(h, Ad, Bd, C, M, N, K, DT[dtype], mode, grid_multiple)
+        torch.cuda.synchronize()
+    finally:
+        pg.pgemm_set_tile_counter(h, None)
+    return si.bits(C.cpu()), (v.cpu().numpy() if v is not None else None), info
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "e4m3fn"])
+def test_workload_256_all_modes(pg, handle, dtype):
+    """fp16 256^3 uniform[-1,1] (seeds 2, 3) and the same shape in bf16 / fp8."""
+    A, B = si.operands(256, 256, 256, dtype, "uniform", workload=1)
+    ref = oracle.gemm(si.bits(A), si.bits(B), dtype)
+    outs = []
+    for mode in MODES:
+        say(f"case 256^3 {dtype} mode {mode}")
+        c, v, info = run(pg, handle, A, B, dtype, mode)
+        err = oracle.normwise_error(c, OUT[dtype][0], ref)
+        assert err <= TOL[dtype], (mode, err)
+        assert info["fast_path"] == 1 and info["tiles"] == 1
+        assert np.array_equal(v, np.ones_like(v)), v
+        outs.append(c)
+    for o in outs[1:]:
+        assert np.array_equal(outs[0], o)
+
+
+SHAPES_INT = [(1, 1, 1), (7, 9, 5), (256, 256, 64), (300, 520, 200), (513, 264, 136), (64, 2048, 640),
+              (1, 784, 48), (259, 16, 1040)]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "e4m3fn"])
+@pytest.mark.parametrize("shape", SHAPES_INT)
+def test_small_integers_bit_exact(pg, handle, dtype, shape):
+    M, N, K = shape
+    A, B = si.operands(M, N, K, dtype, "small_int", workload=7)
+    ref = oracle.gemm(si.bits(A), si.bits(B), dtype)
+    want = oracle.round_to(ref, OUT[dtype][0])
+    for mode in MODES:
+        say(f"case small-int {shape} {dtype} mode {mode}")
+        c, v, info = run(pg, handle, A, B, dtype, mode)
+        assert np.array_equal(c, want), (mode, np.argwhere(c != want)[:5])
+        assert np.array_equal(v[:info["tiles"]], np.ones(info["tiles"], np.int32))
+
+
+SHAPES_RAND = [(1000, 1032, 520), (777, 333, 129), (512, 768, 1024), (257, 1024, 4096)]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "e4m3fn"])
+@pytest.mark.parametrize("shape", SHAPES_RAND)
+def test_uniform_parity(pg, handle, dtype, shape):
+    M, N, K = shape
+    A, B = si.operands(M, N, K, dtype, "uniform", workload=11)
+    ref = oracle.gemm(si.bits(A), si.bits(B), dtype)
+    outs = []
+    for mode in MODES:
+        say(f"case uniform {shape} {dtype} mode {mode}")
+        c, v, info = run(pg, handle, A, B, dtype, mode)
+        err = oracle.normwise_error(c, OUT[dtype][0], ref)
+        assert err <= TOL[dtype], (mode, err)
+        assert np.array_equal(v[:info["tiles"]], np.ones(info["tiles"], np.int32))
+        outs.append(c)
+    for o in outs[1:]:
+        assert np.array_equal(outs[0], o)
+
+
+def test_brute_force_tiny(pg, handle):
+    """Every (M, N, K) in {1..6}^3, every mode, fp16 small integers: bit-exact."""
+    for M in range(1, 7):
+        for N in range(1, 7):
+            for K in range(1, 7):
+                A, B = si.operands(M, N, K, "f16", "small_int", workload=M * 100 + N * 10 + K)
+                want = oracle.round_to(oracle.gemm(si.bits(A), si.bits(B), "f16"), "f16")
+                for mode in MODES:
+                    c, v, _ = run(pg, handle, A, B, "f16", mode)
+                    assert np.array_equal(c, want), (M, N, K, mode)
+                    assert v[0] == 1
+
+
+def test_static_owner_map_and_dynamic_counter(pg, handle):
+    """Static: owner[t] = t mod G (deterministic mapping). Dynamic: every tile once,
+    the work counter back at 0 after each launch, also back to back."""
+    dev = torch.device("cuda:0")
+    M, N, K = 8192, 4096, 64  # 32 x 16 = 512 tiles of 256 x 256
+    A, B = si.operands(M, N, K, "f16", "small_int", workload=3)
+    want = oracle.round_to(oracle.gemm(si.bits(A), si.bits(B), "f16"), "f16")
+    Ad, Bd = A.to(dev), B.to(dev)
+    for gm in (1, 2, 3):
+        info = pg.pgemm_query_launch(handle, M, N, K, 0, 1, gm)
+        T, G = info["tiles"], info["grid"]
+        owner = torch.full((T,), -1, dtype=torch.int32, device=dev)
+        pg.pgemm_set_owner_log(handle, owner)
+        C = torch.empty((M, N), dtype=torch.float16, device=dev)
+        say(f"case owner map static gm={gm} T={T} G={G}")
+        pg.pgemm_run(handle, Ad, Bd, C, M, N, K, 0, 1, gm)
+        torch.cuda.synchronize()
+        pg.pgemm_set_owner_log(handle, None)
+        assert np.array_equal(owner.cpu().numpy(), np.arange(T) % G)
+        assert np.array_equal(si.bits(C.cpu()), want)
+    T = pg.pgemm_query_launch(handle, M, N, K, 0, 2, 0)["tiles"]
+    visits = torch.zeros(T, dtype=torch.int32, device=dev)
+    pg.pgemm_set_tile_counter(handle, visits)
+    try:
+        for rep in range(4):
+            C = torch.empty((M, N), dtype=torch.float16, device=dev)
+            say(f"case dynamic back-to-back rep {rep}")
+            pg.pgemm_run(handle, Ad, Bd, C, M, N, K, 0, 2, 1)
+            pg.pgemm_run(handle, Ad, Bd, C, M, N, K, 0, 2, 0)
+            torch.cuda.synchronize()
+            assert pg.pgemm_read_work_counter(handle) == 0
+            assert np.array_equal(si.bits(C.cpu()), want)
+        assert np.array_equal(visits.cpu().numpy(), np.full(T, 8, np.int32))
+    finally:
+        pg.pgemm_set_tile_counter(handle, None)
+
+
+def test_degenerate_sizes(pg, handle):
+    dev = torch.device("cuda:0")
+    A = torch.ones((5, 0), dtype=torch.float16, device=dev)
+    B = torch.ones((0, 7), dtype=torch.float16, device=dev)
+    C = torch.full((5, 7), 3.0, dtype=torch.float16, device=dev)
+    for mode in MODES:
+        pg.pgemm_run(handle, A, B, C, 5, 7, 0, 0, mode, 0)  # K = 0: an empty sum
+        torch.cuda.synchronize()
+        assert torch.all(C == 0)
+        C.fill_(3.0)
+    pg.pgemm_run(handle, 0, 0, 0, 0, 7, 9, 0, 1, 0)  # M = 0: nothing to do
+    pg.pgemm_run(handle, 0, 0, 0, 5, 0, 9, 0, 1, 0)
+
+
+def test_invalid_arguments(pg, handle):
+    dev = torch.device("cuda:0")
+    A = torch.ones((4, 8), dtype=torch.float16, device=dev)
+    with pytest.raises(pg.PgemmError) as e:
+        pg.pgemm_run(handle, A, A, A, -1, 8, 8, 0, 1, 0)
+    assert e.value.status == pg.PGEMM_ERR_INVALID_ARG
+    with pytest.raises(pg.PgemmError):
+        pg.pgemm_run(handle, A, A, A, 4, 8, 8, 7, 1, 0)
+    with pytest.raises(pg.PgemmError):
+        pg.pgemm_run(handle, A, A, A, 4, 8, 8, 0, 5, 0)
+    with pytest.raises(pg.PgemmError):
+        pg.pgemm_run(handle, 0, A, A, 4, 8, 8, 0, 1, 0)
+    small = torch.zeros(1, dtype=torch.int32, device=dev)
+    pg.pgemm_set_tile_counter(handle, small)
+    try:
+        with pytest.raises(pg.PgemmError):
+            big = torch.zeros((600, 600), dtype=torch.float16, device=dev)
+            pg.pgemm_run(handle, big, big, big, 600, 600, 600, 0, 1, 0)  # 9 tiles > 1 counter
+    finally:
+        pg.pgemm_set_tile_counter(handle, None)
