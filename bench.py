@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Benchmark of the persistent GEMM on one MI355X.
+
+Metric: GEMM TFLOPS (2*M*N*K / time) and its fraction of the dense MFMA
+peak, swept over K, with the non-persistent, static-persistent and
+dynamic-persistent modes side by side (the sweep of the Triton
+persistent-matmul issue, "Describe the issue": M = N = 4096, K from 128
+to 4096 in steps of 128, fp16).
+
+One "step" is one pass of the whole workload: every K of the sweep in
+every scheduling mode, inputs already resident in device memory.
+`value` is the step's total algorithmic flops over its total time.
+
+Prints ONE JSON line on stdout; the per-(K, mode) table goes to
+--table (JSON) when given.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "e4m3fn": 5033.2}  # dense MFMA, 256 CU x 2.4 GHz
+HBM_GBS = 8000.0
+ESIZE = {"f16": 2, "bf16": 2, "e4m3fn": 1}
+MODE_NAMES = {0: "nonpersistent", 1: "static", 2: "dynamic"}
+
+WORKLOADS = {
+    # name: (description, dtype, M, N, K list, modes, grid multiples, input kind, workload id)
+    "sweep4k": ("fp16 GEMM M=N=4096, K=128..4096 step 128, uniform[-1,1], fp32 accumulate, fp16 C; "
+                "non-persistent, static and dynamic persistent per K", "f16", 4096, 4096,
+                list(range(128, 4097, 128)), [0, 1, 2], [0], "uniform", 2),
+    "sweep8k": ("fp16 GEMM M=N=8192, K=256..8192 step 256, uniform[-1,1], fp16 C; non-persistent, and "
+                "static / dynamic persistent at grid multiple 1, 2, 3 x CUs", "f16", 8192, 8192,
+                list(range(256, 8193, 256)), [0, 1, 2], [1, 2, 3], "uniform", 3),
+    "fp8": ("fp8 e4m3 GEMM M=N=K=8192, uniform[-1,1] quantised with scale 1.0, bf16 C; static vs dynamic",
+            "e4m3fn", 8192, 8192, [8192], [0, 1, 2], [0], "uniform", 4),
+    "tail": ("bf16 GEMM M=N=K in {4000, 6144, 8200}, normal(0,1), bf16 C; static vs dynamic (tail effect)",
+             "bf16", None, None, [4000, 6144, 8200], [0, 1, 2], [0], "normal", 5),
+    "square8k": ("fp16 GEMM M=N=K=8192, uniform[-1,1], fp16 C; all modes", "f16", 8192, 8192, [8192],
+                 [0, 1, 2], [0], "uniform", 3),
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="sweep4k", choices=sorted(WORKLOADS))
+    ap.add_argument("--table", default=None, help="write the per-(K, mode) table as JSON here")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample duration")
+    return ap.parse_args()
+
+
+def problems(wl):
+    desc, dtype, M, N, Ks, modes, gms, kind, wid = WORKLOADS[wl]
+    out = []
+    for K in Ks:
+        m = M if M is not None else K
+        n = N if N is not None else K
+        for mode in modes:
+            for gm in (gms if mode != 0 else [0]):
+                out.append((m, n, K, mode, gm))
+    return desc, dtype, kind, wid, out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus_requested": args.gpus}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import persistent_tile_scheduling_macro_amd as pg
+    import seeded_inputs as si
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    desc, dtype, kind, wid, probs = problems(args.workload)
+    dt_code = {"f16": pg.PGEMM_F16, "bf16": pg.PGEMM_BF16, "e4m3fn": pg.PGEMM_F8E4M3_BF16}[dtype]
+    out_dtype = torch.bfloat16 if dtype in ("bf16", "e4m3fn") else torch.float16
+
+    # Inputs: drawn once at the largest shape, sliced per K (leading columns of A, rows of B).
+    shapes = {}
+    for (m, n, K, _, _) in probs:
+        shapes.setdefault((m, n), []).append(K)
+    operands = {}
+    for (m, n), ks in shapes.items():
+        kmax = max(ks)
+        A, B = si.operands(m, n, kmax, dtype, kind, workload=wid)
+        Ad, Bd = A.to(dev), B.to(dev)
+        for K in set(ks):
+            operands[(m, n, K)] = (Ad[:, :K].contiguous(), Bd[:K, :].contiguous())
+        del A, B
+    outs = {(m, n): torch.empty((m, n), dtype=out_dtype, device=dev) for (m, n) in shapes}
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    h = pg.pgemm_create(0)
+    pg.pgemm_set_stream(h, stream)
+
+    def launch(p):
+        m, n, K, mode, gm = p
+        A, B = operands[(m, n, K)]
+        pg.pgemm_run(h, A, B, outs[(m, n)], m, n, K, dt_code, mode, gm)
+
+    # warmup
+    for _ in range(args.warmup):
+        for p in probs:
+            launch(p)
+    torch.cuda.synchronize()
+
+    # timed region: K steps, each the whole workload; one event pair per launch on the
+    # library's stream (torch's current stream)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in probs]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        for i, p in enumerate(probs):
+            ev[s][i][0].record(stream)
+            launch(p)
+            ev[s][i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    flops = {p: 2.0 * p[0] * p[1] * p[2] for p in probs}
+    per = {p: [] for p in probs}
+    for s in range(args.steps):
+        for i, p in enumerate(probs):
+            per[p].append(ev[s][i][0].elapsed_time(ev[s][i][1]) * 1e-3)
+    step_flops = sum(flops.values())
+    value = step_flops * args.steps / wall / 1e12
+    peak = PEAK_TFLOPS[dtype]
+
+    table = []
+    for p in probs:
+        m, n, K, mode, gm = p
+        t = float(np.median(per[p]))
+        info = pg.pgemm_query_launch(h, m, n, K, dt_code, mode, gm)
+        byts = ESIZE[dtype] * (m * K + K * n) + 2 * m * n
+        table.append({"M": m, "N": n, "K": K, "mode": MODE_NAMES[mode], "grid_multiple": gm,
+                      "us": round(t * 1e6, 2), "tflops": round(flops[p] / t / 1e12, 1),
+                      "frac_peak": round(flops[p] / t / 1e12 / peak, 4),
+                      "frac_roofline": round(flops[p] / t / 1e12 / min(peak, flops[p] / byts * HBM_GBS / 1e3), 4),
+                      "tiles": info["tiles"], "grid": info["grid"],
+                      "tiles_per_wg": round(info["tiles"] / info["grid"], 2)})
+
+    # roofline of the dominant kernel (most total time among the three mode kernels)
+    tot = {}
+    for p in probs:
+        tot.setdefault(p[3], [0.0, 0.0, 0])
+        tot[p[3]][0] += sum(per[p])
+        tot[p[3]][1] += flops[p] * len(per[p])
+        tot[p[3]][2] += len(per[p])
+    dom = max(tot, key=lambda k: tot[k][0])
+    dom_time, dom_flops, dom_n = tot[dom]
+    achieved = dom_flops / dom_time / 1e12
+    kernel_names = {0: "gemm_fast_kernel<%s, kNonPersistent>", 1: "gemm_fast_kernel<%s, kStatic>",
+                    2: "gemm_fast_kernel<%s, kDynamic>"}
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": None,
+                "kernel": kernel_names[dom] % {"f16": "kF16", "bf16": "kBF16", "e4m3fn": "kF8E4M3"}[dtype],
+                "launches": dom_n, "avg_us": round(dom_time / dom_n * 1e6, 2),
+                "flops_per_launch_avg": dom_flops / dom_n}
+
+    best = {}
+    for row in table:
+        key = (row["M"], row["N"], row["K"])
+        if key not in best or row["tflops"] > best[key]["tflops"]:
+            best[key] = row
+    mode_tflops = {}
+    for mode in sorted({p[3] for p in probs}):
+        ps = [p for p in probs if p[3] == mode]
+        mode_tflops[MODE_NAMES[mode]] = round(sum(flops[p] for p in ps) / sum(float(np.median(per[p])) for p in ps) / 1e12, 1)
+
+    pg.pgemm_destroy(h)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(dtype, kind, wid, probs, args.cpu_seconds)
+
+    result = {
+        "metric": "GEMM TFLOPS and % of dense MFMA peak vs K; persistent vs non-persistent",
+        "value": round(value, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": dtype if dtype != "e4m3fn" else "e4m3fn->bf16", "data": "synthetic",
+        "config": {"workload": desc, "name": args.workload, "launches_per_step": len(probs),
+                   "flops_per_step": step_flops},
+        "frac_of_peak": round(value / peak, 4),
+        "mode_tflops": mode_tflops,
+        "best": {f"{k[0]}x{k[1]}x{k[2]}": {"mode": v["mode"], "tflops": v["tflops"], "frac_peak": v["frac_peak"]}
+                 for k, v in sorted(best.items())[-3:]},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    if args.table:
+        with open(args.table, "w") as f:
+            json.dump({"result": result, "table": table}, f, indent=1)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(dtype, kind, wid, probs, seconds):
+    """Time the CPU oracle (as it stands) on a bounded row sample of the same workload."""
+    import numpy as np
+
+    import oracle
+    import seeded_inputs as si
+
+    cores = oracle.default_threads()
+    # one mode's worth of distinct (M, N, K) problems, largest K first
+    seen = []
+    for (m, n, K, _, _) in probs:
+        if (m, n, K) not in seen:
+            seen.append((m, n, K))
+    m, n, K = max(seen, key=lambda x: x[2])
+    A, B = si.operands(m, n, K, dtype, kind, workload=wid)
+    Ab, Bb = si.bits(A), si.bits(B)
+    # calibrate on a few rows, then size the sample to about `seconds`
+    rows = np.arange(0, m, max(1, m // 16))[:16]
+    t0 = time.perf_counter()
+    oracle.gemm(Ab, Bb, dtype, rows=rows, nthreads=cores)
+    t_cal = time.perf_counter() - t0
+    per_row = t_cal / len(rows)
+    nrows = int(min(m, max(len(rows), seconds / max(per_row, 1e-9))))
+    rng = np.random.default_rng(0)
+    sample = np.sort(rng.choice(m, size=nrows, replace=False))
+    t0 = time.perf_counter()
+    oracle.gemm(Ab, Bb, dtype, rows=sample, nthreads=cores)
+    t = time.perf_counter() - t0
+    fl = 2.0 * nrows * n * K
+    return {"value": round(fl / t / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{nrows} of {m} rows of the {m}x{n}x{K} {dtype} problem, all {n} columns, "
+                      f"fp64 triple loop, {t:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()
