@@ -56,6 +56,7 @@ def parse():
     ap.add_argument("--table", default=None, help="write the per-(K, mode) table as JSON here")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample duration")
+    ap.add_argument("--modes", default=None, help="comma-separated subset of scheduling modes (0,1,2)")
     return ap.parse_args()
 
 
@@ -88,6 +89,9 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     desc, dtype, kind, wid, probs = problems(args.workload)
+    if args.modes:
+        keep = {int(x) for x in args.modes.split(",")}
+        probs = [p for p in probs if p[3] in keep]
     dt_code = {"f16": pg.PGEMM_F16, "bf16": pg.PGEMM_BF16, "e4m3fn": pg.PGEMM_F8E4M3_BF16}[dtype]
     out_dtype = torch.bfloat16 if dtype in ("bf16", "e4m3fn") else torch.float16
 

@@ -45,7 +45,7 @@ int fail(pgemm_ctx* h, int status, const char* fmt, ...) {
 // the per-dtype translation units).
 constexpr int kFastBM = 256, kFastBN = 256, kFastThreads = 256;
 constexpr int kGenBM = 64, kGenBN = 64, kGenThreads = 256;
-int fast_block_k(int dtype) { return dtype == kF8E4M3 ? 128 : 64; }
+int fast_block_k(int dtype) { return dtype == kF8E4M3 ? 128 : 32; }
 
 kernel_fn pick_kernel(int dtype, int sched, bool fast_path) {
   switch (dtype) {
