@@ -135,9 +135,11 @@ int pgemm_query_launch(pgemm_handle_t h, int64_t M, int64_t N, int64_t K, int dt
                        int grid_multiple, int* tiles, int* grid, int* occupancy, int* bm, int* bn, int* bk,
                        int* fast_path);
 
-/* Tile-order knobs: GROUP_SIZE_M of the grouped order (default 8, the
- * Triton issue's setting; 1 = row-major), and the XCD-aware remap (1 = on,
- * the default; 0 = off). Both apply identically to all modes. */
+/* Tile-order knobs: GROUP_SIZE_M of the grouped order (default 4; the
+ * Triton issue's setting is 8; 1 = row-major), and the XCD-aware remap
+ * (1 = on; 0 = off, the default). Both apply identically to all modes. The
+ * environment variables PGEMM_GROUP_M and PGEMM_XCD_REMAP override the
+ * defaults at pgemm_create. */
 int pgemm_set_tile_order(pgemm_handle_t h, int group_m, int xcd_remap);
 
 /* Host mirror of the device tile order: (pid_m, pid_n) of tile t for an

@@ -1,43 +1,51 @@
 // The fast GEMM kernel for aligned operands (K and N multiples of 16 bytes
 // of elements, 16-byte aligned A and B).
 //
-// Macro tile 256 x 256, 256 threads = 4 waves in a 2 x 2 arrangement, each
-// wave owning a 128 x 128 sub-tile (8 x 8 blocks of 16 x 16 MFMA outputs,
-// 256 fp32 accumulators per lane, kept in AGPRs). K is consumed in steps of
-// BK (32 for fp16/bf16, 128 for fp8: one MFMA k-group per step). Each
-// step's A (256 x BK) and B (BK x 256) slices are copied global -> LDS by
-// buffer loads that write LDS directly (no register staging) into a ring of
-// S stages (4 for 16-bit, 2 for fp8), so copies run S-1 steps ahead of the
-// MFMAs -- the copy/compute overlap of the persistent-kernel forum thread
-// (first answer). Per-CU L2 -> LDS bandwidth on this part is about the rate
-// at which the MFMAs consume a 256 x 256 tile's operands, so the copies
-// must run continuously and well ahead.
+// Macro tile 256 x 256, 512 threads = 8 waves (two per SIMD) in a 2 x 4
+// arrangement, each wave owning a 128 x 64 sub-tile (8 x 4 blocks of
+// 16 x 16 MFMA outputs, 128 fp32 accumulators per lane, kept in AGPRs).
+// K is consumed in steps of 128 bytes of elements (BK = 64 for fp16/bf16,
+// 128 for fp8). Each step's A (256 x BK) and B (BK x 256) slices are
+// copied global -> LDS by buffer loads that write LDS directly (no register
+// staging) into a two-stage ring, so the copy of step s+1 overlaps the
+// MFMAs of step s (the copy/compute overlap of the persistent-kernel forum
+// thread, first answer).
 //
-// Step s on stage c = s mod S:
-//   1. MFMAs for rows 0..3 of the wave's 8 x 8 block grid (fragments of
-//      step s were read into registers during step s-1);
-//   2. wait for this wave's copy of step s+1, then one workgroup barrier:
-//      after it, stage s+1 is complete and nobody reads stage c any more;
-//   3. issue the copy of step s+S into stage c;
-//   4. MFMAs for rows 4..7, interleaved with the LDS reads of step s+1's
-//      fragments (so LDS latency hides under MFMAs at every step).
-// One barrier per step.
+// Why this shape on gfx950 (measured on the part, not taken from the
+// pages): the CU's global -> LDS path moves about 30 B/clk, while a 256 x
+// 256 tile's MFMAs consume 32 B/clk of operands at full rate, so the
+// kernel is bound by that path; copies and MFMAs issued by the same wave
+// overlap poorly, two waves per SIMD overlap them much better; and copy
+// rows must be whole 128-byte lines (half-line rows cut the path's
+// throughput at full occupancy).
+//
+// Step s on stage c = s mod 2:
+//   1. wait for this wave's copy of step s, one workgroup barrier: stage c
+//      is complete and nobody reads stage c^1 any more;
+//   2. issue the copy of step s+1 into stage c^1, two instructions after
+//      each of the first four MFMA rows, so it starts as early as possible;
+//   3. MFMAs of the step's k-groups; the LDS reads of k-group kk+1 are
+//      issued while the MFMAs of k-group kk run.
+// (A variant with a second barrier per step, freeing each stage as soon as
+// its fragments are in registers so copies get two steps of lead, measured
+// slower on this part: the extra barrier costs more than the lead buys.)
 //
 // All three scheduling modes run this one body over the flattened sequence
-// of (tile, k-step) pairs their scheduler produces. The copies cross tile
-// boundaries freely, so in the persistent modes the next tile's first
-// S-1 steps are in flight while the current tile's epilogue converts and
-// stores C -- the pipelining across output tiles that the Triton
-// persistent-matmul issue ("Describe the issue") expected persistence to
-// buy. In the non-persistent mode a workgroup owns one tile.
+// of (tile, k-step) pairs their scheduler produces. Copies cross tile
+// boundaries freely, so in the persistent modes the next tile's first copy
+// is in flight while the current tile's epilogue converts and stores C --
+// the pipelining across output tiles the Triton persistent-matmul issue
+// ("Describe the issue") expected persistence to buy. In the
+// non-persistent mode a workgroup owns one tile.
 //
-// LDS layouts use 16-byte chunks, swizzled so that every fragment read is
-// bank-conflict-free on gfx950 (64 banks; ds_read_b128 serves lanes
-// {0-7,16-23}, {8-15,24-31}, ... per pass; transpose reads serve 32 lanes):
-//   A, 16-bit: 256 rows (m) x 64 B; chunk c of row r at c ^ ((r >> 1) & 3).
+// LDS layouts use 16-byte chunks, swizzled so that the fragment reads are
+// bank-conflict-free on gfx950 (measured: 64 banks; ds_read_b128 serves
+// lanes {0-7,16-23}, {8-15,24-31}, ... per pass; transpose reads serve 32
+// lanes per pass):
+//   A, 16-bit: 256 rows (m) x 128 B; chunk c of row r at c ^ (r & 7).
 //   A, fp8:    256 rows (m) x 128 B; chunk c of row r at c ^ sa8(r),
 //              sa8(r) = ((r >> 1) & 1) | (r & 4).
-//   B, 16-bit: 32 rows (k) x 512 B; chunk c of row r at
+//   B, 16-bit: 64 rows (k) x 512 B; chunk c of row r at
 //              c ^ (2*(r & 3) + 8*((r >> 3) & 1)).
 //   B, fp8:    128 rows (k) x 256 B; chunk c of row r at
 //              c ^ ((r & 7) + 8*((r >> 5) & 1)).
@@ -55,10 +63,10 @@
 namespace pgemm {
 namespace fast {
 
-constexpr int BM = 256, BN = 256, THREADS = 256;
+constexpr int BM = 256, BN = 256, THREADS = 512;
+constexpr int WAVES = THREADS / 64;
 
-__host__ __device__ constexpr int block_k(int esize) { return esize == 2 ? 32 : 128; }
-__host__ __device__ constexpr int stages(int esize) { return esize == 2 ? 4 : 2; }
+__host__ __device__ constexpr int block_k(int esize) { return 128 / esize; }
 
 template <int DT>
 struct Frag;
@@ -111,105 +119,99 @@ __device__ inline typename Frag<DT>::t read_a(const uint8_t* lo, const uint8_t* 
 template <int DT, int SCHED>
 __global__ void __launch_bounds__(THREADS) gemm_fast_kernel(Params p) {
   constexpr int ES = Traits<DT>::esize;
-  constexpr int BK = block_k(ES);      // k elements per step
-  constexpr int S = stages(ES);        // LDS ring depth
-  constexpr int A_ROW = BK * ES;       // bytes per A row in LDS (64 or 128)
-  constexpr int A_BYTES = BM * A_ROW;  // per stage
-  constexpr int B_ROW = BN * ES;       // bytes per B row in LDS (512 or 256)
-  constexpr int B_BYTES = BK * B_ROW;  // per stage
+  constexpr int BK = block_k(ES);                // k elements per step
+  constexpr int KSUB = BK / Traits<DT>::kgroup;  // MFMA k-groups per step (2 or 1)
+  constexpr int A_ROW = 128;                     // bytes per A row in LDS
+  constexpr int A_BYTES = BM * A_ROW;            // 32 KiB per stage
+  constexpr int B_ROW = BN * ES;                 // bytes per B row in LDS (512 or 256)
+  constexpr int B_BYTES = BK * B_ROW;            // 32 KiB per stage
   constexpr int LA = A_BYTES / (THREADS * 16), LB = B_BYTES / (THREADS * 16);
-  constexpr int L = LA + LB;           // copy instructions per thread per step
-  constexpr int A_RPI = 1024 / A_ROW;  // A rows per copy instruction (16 or 8)
-  static_assert(S == 2 || S == 4, "ring depth");
-  static_assert((S - 1) * L < 64, "vmcnt range");
+  constexpr int L = LA + LB;                     // copy instructions per thread per step
+  static_assert(LA == 4 && LB == 4, "copy split assumes 4 + 4 instructions per step");
   typedef typename Traits<DT>::out_t out_t;
   typedef typename Frag<DT>::t frag_t;
   typedef std::integral_constant<int, 0> I0;
   typedef std::integral_constant<int, 1> I1;
-  typedef std::integral_constant<int, (S > 2 ? 2 : 0)> I2;
-  typedef std::integral_constant<int, (S > 2 ? 3 : 1)> I3;
 
   __shared__ __attribute__((aligned(1024))) uint8_t sA0[A_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t sB0[B_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t sA1[A_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t sB1[B_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t sA2[S > 2 ? A_BYTES : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB2[S > 2 ? B_BYTES : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t sA3[S > 2 ? A_BYTES : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB3[S > 2 ? B_BYTES : 16];
   __shared__ int s_ring[8]; // dynamic mode: tile id of tile-sequence number q at q % 8
 
   auto bufA = [&](auto c) __attribute__((always_inline)) -> uint8_t* {
-    constexpr int C = decltype(c)::value;
-    return C == 0 ? sA0 : C == 1 ? sA1 : C == 2 ? sA2 : sA3;
+    return decltype(c)::value == 0 ? sA0 : sA1;
   };
   auto bufB = [&](auto c) __attribute__((always_inline)) -> uint8_t* {
-    constexpr int C = decltype(c)::value;
-    return C == 0 ? sB0 : C == 1 ? sB1 : C == 2 ? sB2 : sB3;
+    return decltype(c)::value == 0 ? sB0 : sB1;
   };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // wave-uniform, lives in an SGPR
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;                   // 2 x 4 waves of 128 x 64
   const int M = p.M, N = p.N, K = p.K, T = p.T, G = p.G;
-  // k-steps per tile, rounded up to a multiple of S so that every tile starts
-  // on stage 0 (the extra steps read zeros: they lie past K)
-  const int nk = ((K + BK - 1) / BK + S - 1) / S * S;
+  // k-steps per tile, rounded up to even so that every tile starts on stage
+  // 0 (an extra step reads zeros: it lies past K)
+  const int nk = ((K + BK - 1) / BK + 1) & ~1;
   const int64_t lda = (int64_t)K * ES; // bytes per row of A
   const int64_t ldb = (int64_t)N * ES; // bytes per row of B
   const int64_t ldc = N;               // elements per row of C
 
   // ---- per-lane constants of the global -> LDS copy ------------------------
-  // A: instruction q = wave + 4j covers A_RPI rows; lane -> row q*A_RPI +
-  // lane/(A_ROW/16), physical chunk lane % (A_ROW/16); the swizzle depends
-  // on the row's low bits only, which are lane-constant.
-  int a_row0, a_chunk;
+  // Instruction q = wave + 8j fills one 1 KiB block of a stage: A rows
+  // 8q..8q+7 (lane -> row 8q + lane/8, physical chunk lane % 8); B rows
+  // 2q, 2q+1 (16-bit) or 4q..4q+3 (fp8). The swizzles depend on row bits
+  // that are constant per lane and wave (fp8 B: and on the parity of j).
+  const int a_row0 = 8 * wave + (lane >> 3); // + 64 j
+  int a_chunk;
   if constexpr (ES == 2) {
-    a_row0 = A_RPI * wave + (lane >> 2);
-    a_chunk = (lane & 3) ^ ((lane >> 3) & 3); // row & 15 == lane >> 2
+    a_chunk = (lane & 7) ^ (lane >> 3);
   } else {
-    a_row0 = A_RPI * wave + (lane >> 3);
-    const int r = lane >> 3;                  // row & 7
+    const int r = lane >> 3;
     a_chunk = (lane & 7) ^ (((r >> 1) & 1) | (r & 4));
   }
-  // B: instruction q = wave + 4j covers 1024 / B_ROW rows.
-  int b_row0, b_pchunk, b_h0;
+  int b_row0, b_chunk0, b_chunk1;
   if constexpr (ES == 2) {
-    b_row0 = 2 * wave + (lane >> 5);
-    b_pchunk = lane & 31;
-    b_h0 = 2 * (b_row0 & 3); // + 8 * (j & 1) per instruction
+    b_row0 = 2 * wave + (lane >> 5); // + 16 j
+    const int h = 2 * (b_row0 & 3) + 8 * ((wave >> 2) & 1);
+    b_chunk0 = (lane & 31) ^ h;
+    b_chunk1 = b_chunk0;
   } else {
-    b_row0 = 4 * wave + (lane >> 4);
-    b_pchunk = lane & 15;
-    b_h0 = b_row0 & 7;       // + 8 * ((j >> 1) & 1) per instruction
+    b_row0 = 4 * wave + (lane >> 4); // + 32 j
+    const int h = b_row0 & 7;        // + 8 for odd j
+    b_chunk0 = (lane & 15) ^ h;
+    b_chunk1 = (lane & 15) ^ (h + 8);
   }
 
   // ---- per-lane constants of the fragment reads ----------------------------
   const int g = lane >> 4, s16 = lane & 15;
-  int a_off[2];
+  int a_off[KSUB][2];
   {
     const int r = wm * 128 + s16; // + mb * 16
-    if constexpr (ES == 2) {
-      a_off[0] = r * A_ROW + 16 * (g ^ ((s16 >> 1) & 3));
-      a_off[1] = a_off[0];
-    } else {
-      const int sw = ((s16 >> 1) & 1) | (s16 & 4);
-      a_off[0] = r * A_ROW + 16 * ((2 * g) ^ sw);
-      a_off[1] = r * A_ROW + 16 * ((2 * g + 1) ^ sw);
+#pragma unroll
+    for (int kk = 0; kk < KSUB; ++kk) {
+      if constexpr (ES == 2) {
+        a_off[kk][0] = r * A_ROW + 16 * ((4 * kk + g) ^ (s16 & 7));
+        a_off[kk][1] = a_off[kk][0];
+      } else {
+        const int sw = ((s16 >> 1) & 1) | (s16 & 4);
+        a_off[kk][0] = r * A_ROW + 16 * ((2 * g) ^ sw);
+        a_off[kk][1] = r * A_ROW + 16 * ((2 * g + 1) ^ sw);
+      }
     }
   }
-  int b_off[8];
+  int b_off[4];
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) {
+  for (int nb = 0; nb < 4; ++nb) {
     if constexpr (ES == 2) {
-      const int k = 8 * g + (s16 >> 2); // +4 for the second read
-      const int Lc = wn * 16 + 2 * nb + ((s16 & 3) >> 1);
+      const int k = 8 * g + (s16 >> 2); // + 32 kk, +4 for the second read
+      const int Lc = wn * 8 + 2 * nb + ((s16 & 3) >> 1);
       const int h = 2 * (s16 >> 2) + 8 * (g & 1);
       b_off[nb] = k * B_ROW + 16 * (Lc ^ h) + 8 * (s16 & 1);
     } else {
       const int k = 32 * g + (s16 >> 1); // +8, +16, +24 for reads 1..3
-      const int Lc = wn * 8 + nb;
+      const int Lc = wn * 4 + nb;
       const int h = (s16 >> 1) + 8 * (g & 1);
       b_off[nb] = k * B_ROW + 16 * (Lc ^ h) + 8 * (s16 & 1);
     }
@@ -218,8 +220,8 @@ __global__ void __launch_bounds__(THREADS) gemm_fast_kernel(Params p) {
   // ---- the tile sequence of this workgroup ---------------------------------
   // Sequence number q -> tile id. Static: blockIdx + q*G; non-persistent:
   // blockIdx for q = 0 only; dynamic: blockIdx for q = 0, then each tile's
-  // successor is claimed when the producer starts copying that tile, and
-  // published in s_ring before the next barrier.
+  // successor is claimed when the producer starts copying that tile and is
+  // published in s_ring at the end of that step, before the next barrier.
   int claim_val = 0;
   bool claim_pending = false; // thread 0 only: a claim waiting to be published
   int claim_seq = 0;          // sequence number the pending claim is for
@@ -242,19 +244,17 @@ __global__ void __launch_bounds__(THREADS) gemm_fast_kernel(Params p) {
     }
   };
 
-  // ---- producer: copy of step `issued` into stage `issued % S` --------------
-  // A copy is begun (tile and k of the step resolved, buffer resources
-  // built) and then issued one 1 KiB instruction at a time, interleaved
-  // with the MFMAs: a burst of copy instructions would stall this wave's
-  // in-order issue behind the memory pipeline and starve the MFMAs.
+  // ---- producer: the copy of step `issued` ----------------------------------
+  // begin_copy() resolves the step's tile and k and builds the buffer
+  // resources; copy_part<J>() issues its J-th 1 KiB instruction.
   int issued = 0;      // copies begun
   int p_tile = 0;      // tile of the copy in progress
   bool p_done = false; // no more steps to copy
-  bool p_busy = false; // a begun copy still has instructions to issue
+  bool p_busy = false; // the begun copy has instructions left
   __amdgpu_buffer_rsrc_t ra, rb;
   bool p_kval = false;
   int p_mrem = 0, p_krem = 0, p_nrem = 0;
-  uint32_t a_base = 0;
+  const uint32_t a_base = (uint32_t)a_row0 * (uint32_t)lda + 16u * (uint32_t)a_chunk;
   auto begin_copy = [&]() __attribute__((always_inline)) {
     if (p_done) return;
     const int q = issued / nk, kt = issued - q * nk;
@@ -265,7 +265,7 @@ __global__ void __launch_bounds__(THREADS) gemm_fast_kernel(Params p) {
         return;
       }
       if constexpr (SCHED == kDynamic) {
-        if (tid == 0) { // claim the successor now; published before the next barrier
+        if (tid == 0) { // claim the successor now; published after this step's MFMAs
           claim_val = claim_tile(p.counter, T, G);
           claim_seq = q + 1;
           claim_pending = true;
@@ -275,88 +275,68 @@ __global__ void __launch_bounds__(THREADS) gemm_fast_kernel(Params p) {
     int pm, pn;
     tile_coords(p_tile, p, &pm, &pn);
     const int m0 = pm * BM, n0 = pn * BN, k0 = kt * BK;
-    // A rebased at (m0, k0), B at (k0, n0); rows past M or K and chunks
-    // past K or N read zeros.
+    // A rebased at (m0, k0), B at (k0, n0); rows past M or K and chunks past
+    // K or N read zeros.
     ra = make_rsrc(p.A + (int64_t)m0 * lda + (int64_t)k0 * ES);
     rb = make_rsrc(p.B + (int64_t)k0 * ldb + (int64_t)n0 * ES);
     p_mrem = M - m0;
     p_krem = K - k0;
     p_nrem = (N - n0) * ES;
     p_kval = (k0 * ES + 16 * a_chunk) < K * ES;
-    a_base = (uint32_t)a_row0 * (uint32_t)lda + 16u * (uint32_t)a_chunk;
     p_busy = true;
     ++issued;
   };
-  // instruction j (0 <= j < LA + LB) of the copy in progress, into stage (sA, sB)
   auto copy_part = [&](uint8_t* sA, uint8_t* sB, auto jc) __attribute__((always_inline)) {
     constexpr int J = decltype(jc)::value;
     if (!p_busy) return;
     if constexpr (J < LA) {
-      const bool ok = p_kval & (a_row0 + 4 * A_RPI * J < p_mrem);
-      const uint32_t off = ok ? a_base + (uint32_t)(4 * A_RPI * J) * (uint32_t)lda : kOOB;
-      load16_to_lds(ra, sA + (wave + 4 * J) * 1024, off);
+      const bool ok = p_kval & (a_row0 + 64 * J < p_mrem);
+      const uint32_t off = ok ? a_base + (uint32_t)(64 * J) * (uint32_t)lda : kOOB;
+      load16_to_lds(ra, sA + (wave + WAVES * J) * 1024, off);
     } else {
       constexpr int JB = J - LA;
       int row, Lc;
       if constexpr (ES == 2) {
-        row = b_row0 + 8 * JB;
-        Lc = b_pchunk ^ (b_h0 + 8 * (JB & 1));
-      } else {
         row = b_row0 + 16 * JB;
-        Lc = b_pchunk ^ (b_h0 + 8 * ((JB >> 1) & 1));
+        Lc = b_chunk0;
+      } else {
+        row = b_row0 + 32 * JB;
+        Lc = (JB & 1) ? b_chunk1 : b_chunk0;
       }
       const bool ok = (row < p_krem) & (16 * Lc < p_nrem);
       const uint32_t off = ok ? (uint32_t)row * (uint32_t)ldb + 16u * (uint32_t)Lc : kOOB;
-      load16_to_lds(rb, sB + (wave + 4 * JB) * 1024, off);
+      load16_to_lds(rb, sB + (wave + WAVES * JB) * 1024, off);
     }
-    if (J == LA + LB - 1) p_busy = false;
+    if (J == L - 1) p_busy = false;
   };
-  // a whole copy at once (prologue only)
-  auto copy_all = [&](auto c) __attribute__((always_inline)) {
-    begin_copy();
-    uint8_t* sA = bufA(c);
-    uint8_t* sB = bufB(c);
-    copy_part(sA, sB, std::integral_constant<int, 0>{});
-    copy_part(sA, sB, std::integral_constant<int, 1>{});
-    copy_part(sA, sB, std::integral_constant<int, 2>{});
-    copy_part(sA, sB, std::integral_constant<int, 3>{});
-    copy_part(sA, sB, std::integral_constant<int, 4>{});
-    copy_part(sA, sB, std::integral_constant<int, 5>{});
-    copy_part(sA, sB, std::integral_constant<int, 6>{});
-    copy_part(sA, sB, std::integral_constant<int, 7>{});
-    if constexpr (L > 8) {
-      copy_part(sA, sB, std::integral_constant<int, (L > 8 ? 8 : 0)>{});
-      copy_part(sA, sB, std::integral_constant<int, (L > 8 ? 9 : 0)>{});
-      copy_part(sA, sB, std::integral_constant<int, (L > 8 ? 10 : 0)>{});
-      copy_part(sA, sB, std::integral_constant<int, (L > 8 ? 11 : 0)>{});
-      copy_part(sA, sB, std::integral_constant<int, (L > 8 ? 12 : 0)>{});
-      copy_part(sA, sB, std::integral_constant<int, (L > 8 ? 13 : 0)>{});
-      copy_part(sA, sB, std::integral_constant<int, (L > 8 ? 14 : 0)>{});
-      copy_part(sA, sB, std::integral_constant<int, (L > 8 ? 15 : 0)>{});
-    }
+  auto copy_pair = [&](auto c, auto pc) __attribute__((always_inline)) {
+    constexpr int P = decltype(pc)::value;
+    copy_part(bufA(c), bufB(c), std::integral_constant<int, 2 * P>{});
+    copy_part(bufA(c), bufB(c), std::integral_constant<int, 2 * P + 1>{});
   };
 
   // ---- accumulators and fragments -------------------------------------------
-  floatx4_t acc[8][8];
-  frag_t af[2][8], bf[2][8];
+  floatx4_t acc[8][4];
+  frag_t af[2][8], bf[2][4];
   auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < 4; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
     acc_drain(); // accvgpr writes -> MFMA srcC reads
   };
-  auto read_frags = [&](auto f, auto c, int mb) __attribute__((always_inline)) {
+  auto read_a_frag = [&](auto f, const uint8_t* sA, int kk, int mb) __attribute__((always_inline)) {
     constexpr int F = decltype(f)::value;
-    const uint8_t* sA = bufA(c);
-    const uint8_t* sB = bufB(c);
-    bf[F][mb] = read_b<DT>(sB + b_off[mb]);
-    af[F][mb] = read_a<DT>(sA + a_off[0] + mb * 16 * A_ROW, sA + a_off[1] + mb * 16 * A_ROW);
+    af[F][mb] = read_a<DT>(sA + a_off[kk][0] + mb * 16 * A_ROW, sA + a_off[kk][1] + mb * 16 * A_ROW);
+  };
+  auto read_b_frag = [&](auto f, const uint8_t* sB, int kk, int nb) __attribute__((always_inline)) {
+    constexpr int F = decltype(f)::value;
+    bf[F][nb] = read_b<DT>(sB + b_off[nb] + kk * 32 * B_ROW);
   };
   auto mfma_row = [&](auto f, int mb) __attribute__((always_inline)) {
     constexpr int F = decltype(f)::value;
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) mfma_acc(acc[mb][nb], bf[F][nb], af[F][mb]);
+    for (int nb = 0; nb < 4; ++nb) mfma_acc(acc[mb][nb], bf[F][nb], af[F][mb]);
   };
 
   // ---- epilogue: round to the output type and store one tile ---------------
@@ -365,14 +345,14 @@ __global__ void __launch_bounds__(THREADS) gemm_fast_kernel(Params p) {
     int pm, pn;
     tile_coords(tile, p, &pm, &pn);
     const int mrow = pm * BM + wm * 128 + s16;
-    const int ncol = pn * BN + wn * 128 + 4 * g;
+    const int ncol = pn * BN + wn * 64 + 4 * g;
     out_t* C = reinterpret_cast<out_t*>(p.C);
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
       const int m = mrow + mb * 16;
       if (m < M) {
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
+        for (int nb = 0; nb < 4; ++nb) {
           const int n = ncol + nb * 16;
           out_t* dst = C + (int64_t)m * ldc + n;
           if (n + 3 < N) {
@@ -391,107 +371,63 @@ __global__ void __launch_bounds__(THREADS) gemm_fast_kernel(Params p) {
     }
   };
 
-  // ---- prologue: copies of steps 0..S-1, fragments of step 0 ----------------
-  // nk is a multiple of S, so all S prologue copies belong to the first tile
-  copy_all(I0{});
-  copy_all(I1{});
-  if constexpr (S > 2) {
-    copy_all(I2{});
-    copy_all(I3{});
-  }
-  publish_claim();
-  // step 0's copy is the oldest; `issued - 1` newer steps may stay in flight
-  if (issued == S) {
-    wait_vmcnt<(S - 1) * L>();
-  } else {
-    wait_vmcnt<0>();
-  }
-  __syncthreads();
-  zero_acc();
-#pragma unroll
-  for (int mb = 0; mb < 8; ++mb) read_frags(I0{}, I0{}, mb);
-
-  int cs = 0;           // consumer step
-  bool stores_pending = false;
+  // ---- one k-step on stage C --------------------------------------------------
   bool has_next = true;
-
-  // One consumer step on stage C (compile time), fragment set C & 1.
-  // Copy instructions: the second half of the copy begun in the previous
-  // step (into stage C-1) rides along rows 0..3; the first half of the copy
-  // begun at this step's barrier (into stage C) rides along rows 4..7.
-  constexpr int HALF = L / 2;       // copy instructions per half step (4 or 8)
-  constexpr int PER_ROW = HALF / 4; // per MFMA row (1 or 2)
   auto step = [&](auto cst) __attribute__((always_inline)) {
     constexpr int C = decltype(cst)::value;
-    constexpr int F = C & 1, FN = F ^ 1, CN = (C + 1) % S, CP = (C + S - 1) % S;
-    typedef std::integral_constant<int, F> IF;
-    typedef std::integral_constant<int, FN> IFN;
-    typedef std::integral_constant<int, CN> ICN;
-    typedef std::integral_constant<int, CP> ICP;
-    typedef std::integral_constant<int, C> IC;
-    has_next = issued > cs + 1;
-    auto first_row = [&](auto mbc) __attribute__((always_inline)) {
-      constexpr int MB = decltype(mbc)::value;
-      mfma_row(IF{}, MB);
-      copy_part(bufA(ICP{}), bufB(ICP{}), std::integral_constant<int, HALF + PER_ROW * MB>{});
-      if constexpr (PER_ROW > 1)
-        copy_part(bufA(ICP{}), bufB(ICP{}), std::integral_constant<int, HALF + PER_ROW * MB + PER_ROW - 1>{});
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    first_row(std::integral_constant<int, 0>{});
-    first_row(std::integral_constant<int, 1>{});
-    first_row(std::integral_constant<int, 2>{});
-    first_row(std::integral_constant<int, 3>{});
-    if (has_next) {
-      // wait for this wave's copy of step cs+1 (newer copies may stay in flight)
-      const int after = issued - (cs + 2); // steps copied after step cs+1
-      if (stores_pending || after <= 0) {
-        wait_vmcnt<0>();
-        stores_pending = false;
-      } else if (S == 4 && after >= 2) {
-        wait_vmcnt<(S == 4 ? 2 * L : 0)>();
-      } else {
-        wait_vmcnt<L>();
+    typedef std::integral_constant<int, C ^ 1> ICN;
+    const uint8_t* sA = bufA(cst);
+    const uint8_t* sB = bufB(cst);
+    wait_vmcnt<0>(); // this wave's copy of this step (and any older stores) landed
+    __syncthreads(); // ... every wave's; nobody reads stage C^1 any more
+    begin_copy();    // the next step, into stage C^1
+    has_next = p_busy;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) read_b_frag(I0{}, sB, 0, nb);
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) read_a_frag(I0{}, sA, 0, mb);
+    auto kgroup = [&](auto fc, int kk) __attribute__((always_inline)) {
+      typedef std::integral_constant<int, decltype(fc)::value ^ 1> IFN;
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) {
+        mfma_row(fc, mb);
+        if (kk + 1 < KSUB) { // the next k-group's fragments ride along
+          if (mb < 4) read_b_frag(IFN{}, sB, kk + 1, mb);
+          read_a_frag(IFN{}, sA, kk + 1, mb);
+        }
+        if (kk == 0) { // the next step's copy: two instructions after each of rows 0..3
+          if (mb == 0) copy_pair(ICN{}, std::integral_constant<int, 0>{});
+          if (mb == 1) copy_pair(ICN{}, std::integral_constant<int, 1>{});
+          if (mb == 2) copy_pair(ICN{}, std::integral_constant<int, 2>{});
+          if (mb == 3) copy_pair(ICN{}, std::integral_constant<int, 3>{});
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __syncthreads();
-      begin_copy(); // step cs + S into stage C, which nobody reads any more
-    }
-    // the next step's fragments (harmless stale reads when there is no next step)
-    auto second_row = [&](auto mbc) __attribute__((always_inline)) {
-      constexpr int MB = decltype(mbc)::value; // 4..7
-      read_frags(IFN{}, ICN{}, 2 * (MB - 4));
-      mfma_row(IF{}, MB);
-      copy_part(bufA(IC{}), bufB(IC{}), std::integral_constant<int, PER_ROW * (MB - 4)>{});
-      if constexpr (PER_ROW > 1)
-        copy_part(bufA(IC{}), bufB(IC{}), std::integral_constant<int, PER_ROW * (MB - 4) + PER_ROW - 1>{});
-      read_frags(IFN{}, ICN{}, 2 * (MB - 4) + 1);
-      __builtin_amdgcn_sched_barrier(0);
     };
-    second_row(std::integral_constant<int, 4>{});
-    second_row(std::integral_constant<int, 5>{});
-    second_row(std::integral_constant<int, 6>{});
-    second_row(std::integral_constant<int, 7>{});
-    publish_claim();
-    ++cs;
+    kgroup(I0{}, 0);
+    if constexpr (KSUB > 1) kgroup(I1{}, 1);
+    publish_claim(); // the claim made by begin_copy has had a whole step to return
   };
 
+  // ---- the (tile, k-step) pipeline -----------------------------------------
+  begin_copy(); // step 0 into stage 0
+  copy_pair(I0{}, std::integral_constant<int, 0>{});
+  copy_pair(I0{}, std::integral_constant<int, 1>{});
+  copy_pair(I0{}, std::integral_constant<int, 2>{});
+  copy_pair(I0{}, std::integral_constant<int, 3>{});
+  publish_claim();
   int c_q = 0; // consumer tile sequence number
   int c_tile = blockIdx.x;
   for (;;) {
-    for (int kt = 0; kt < nk; kt += S) {
+    zero_acc();
+    for (int kt = 0; kt < nk; kt += 2) {
       step(I0{});
       step(I1{});
-      if constexpr (S > 2) {
-        step(I2{});
-        step(I3{});
-      }
     }
-    // tile finished: store it while the next tile's copies are in flight
+    // tile finished: store it while the next tile's first copy is in flight
     epilogue(c_tile);
-    stores_pending = true;
     if (!has_next) break;
     c_tile = tile_of(++c_q);
-    zero_acc();
   }
 }
 

@@ -24,8 +24,11 @@ struct pgemm_ctx {
   int64_t n_visits = 0;
   int32_t* owner = nullptr;
   int64_t n_owner = 0;
-  int group_m = 8;
-  int xcd_remap = 1;
+  // Tile-order defaults measured on MI355X (8192^3 and 4096^3 fp16, round-robin
+  // timing): the XCD remap did not help and GROUP_SIZE_M between 1 and 16 moved
+  // throughput by a few percent at most.
+  int group_m = 4;
+  int xcd_remap = 0;
   char last_error[512] = {0};
 };
 
@@ -43,9 +46,9 @@ int fail(pgemm_ctx* h, int status, const char* fmt, ...) {
 
 // Macro-tile facts of the two kernel bodies (the kernels themselves live in
 // the per-dtype translation units).
-constexpr int kFastBM = 256, kFastBN = 256, kFastThreads = 256;
+constexpr int kFastBM = 256, kFastBN = 256, kFastThreads = 512;
 constexpr int kGenBM = 64, kGenBN = 64, kGenThreads = 256;
-int fast_block_k(int dtype) { return dtype == kF8E4M3 ? 128 : 32; }
+int fast_block_k(int dtype) { return dtype == kF8E4M3 ? 128 : 64; }
 
 kernel_fn pick_kernel(int dtype, int sched, bool fast_path) {
   switch (dtype) {
