@@ -19,16 +19,21 @@
 // rows must be whole 128-byte lines (half-line rows cut the path's
 // throughput at full occupancy).
 //
-// Step s on stage c = s mod 2:
-//   1. wait for this wave's copy of step s, one workgroup barrier: stage c
-//      is complete and nobody reads stage c^1 any more;
-//   2. issue the copy of step s+1 into stage c^1, two instructions after
-//      each of the first four MFMA rows, so it starts as early as possible;
-//   3. MFMAs of the step's k-groups; the LDS reads of k-group kk+1 are
-//      issued while the MFMAs of k-group kk run.
-// (A variant with a second barrier per step, freeing each stage as soon as
-// its fragments are in registers so copies get two steps of lead, measured
-// slower on this part: the extra barrier costs more than the lead buys.)
+// Step s on stage c = s mod 2 (16-bit: two MFMA k-groups per step):
+//   1. MFMAs of k-group 0 (fragments read during step s-1) while the
+//      fragments of k-group 1 are read from stage c;
+//   2. wait for this wave's copy of step s+1, one workgroup barrier: stage
+//      c^1 is complete, and every wave has read all of stage c;
+//   3. issue the copy of step s+2 into stage c, two instructions after each
+//      of the next four MFMA rows;
+//   4. MFMAs of k-group 1 while the k-group-0 fragments of step s+1 are
+//      read from stage c^1.
+// So every LDS read has MFMAs to hide behind, and there is one barrier per
+// step. fp8 steps are a single k-group: the barrier sits at the top of the
+// step, the next copy is issued right after it, and the step's fragments
+// are read after it. (A variant with a second barrier per step, freeing
+// each stage as soon as its fragments are in registers, measured slower on
+// this part: the extra barrier costs more than the earlier copies buy.)
 //
 // All three scheduling modes run this one body over the flattened sequence
 // of (tile, k-step) pairs their scheduler produces. Copies cross tile
@@ -372,50 +377,97 @@ __global__ void __launch_bounds__(THREADS) gemm_fast_kernel(Params p) {
   };
 
   // ---- one k-step on stage C --------------------------------------------------
+  int cs = 0; // consumer step
   bool has_next = true;
-  auto step = [&](auto cst) __attribute__((always_inline)) {
+  // fp8 step: barrier at the top, next copy right after it.
+  auto step_top = [&](auto cst) __attribute__((always_inline)) {
     constexpr int C = decltype(cst)::value;
     typedef std::integral_constant<int, C ^ 1> ICN;
     const uint8_t* sA = bufA(cst);
     const uint8_t* sB = bufB(cst);
-    wait_vmcnt<0>(); // this wave's copy of this step (and any older stores) landed
-    __syncthreads(); // ... every wave's; nobody reads stage C^1 any more
-    begin_copy();    // the next step, into stage C^1
+    wait_vmcnt<0>();
+    __syncthreads();
+    begin_copy();
     has_next = p_busy;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) read_b_frag(I0{}, sB, 0, nb);
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) read_a_frag(I0{}, sA, 0, mb);
-    auto kgroup = [&](auto fc, int kk) __attribute__((always_inline)) {
-      typedef std::integral_constant<int, decltype(fc)::value ^ 1> IFN;
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb) {
-        mfma_row(fc, mb);
-        if (kk + 1 < KSUB) { // the next k-group's fragments ride along
-          if (mb < 4) read_b_frag(IFN{}, sB, kk + 1, mb);
-          read_a_frag(IFN{}, sA, kk + 1, mb);
-        }
-        if (kk == 0) { // the next step's copy: two instructions after each of rows 0..3
-          if (mb == 0) copy_pair(ICN{}, std::integral_constant<int, 0>{});
-          if (mb == 1) copy_pair(ICN{}, std::integral_constant<int, 1>{});
-          if (mb == 2) copy_pair(ICN{}, std::integral_constant<int, 2>{});
-          if (mb == 3) copy_pair(ICN{}, std::integral_constant<int, 3>{});
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
-    kgroup(I0{}, 0);
-    if constexpr (KSUB > 1) kgroup(I1{}, 1);
-    publish_claim(); // the claim made by begin_copy has had a whole step to return
+    for (int mb = 0; mb < 8; ++mb) {
+      mfma_row(I0{}, mb);
+      if (mb == 0) copy_pair(ICN{}, std::integral_constant<int, 0>{});
+      if (mb == 1) copy_pair(ICN{}, std::integral_constant<int, 1>{});
+      if (mb == 2) copy_pair(ICN{}, std::integral_constant<int, 2>{});
+      if (mb == 3) copy_pair(ICN{}, std::integral_constant<int, 3>{});
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    publish_claim();
+    ++cs;
+  };
+  // mid-step variant (16-bit): the barrier sits between the two k-groups.
+  // Before it: MFMAs of k-group 0 while k-group 1's fragments are read.
+  // After it: the copy of step s+2 goes into this (now free) stage and the
+  // next step's k-group-0 fragments are read during k-group 1's MFMAs.
+  auto step_mid = [&](auto cst) __attribute__((always_inline)) {
+    constexpr int C = decltype(cst)::value;
+    typedef std::integral_constant<int, C ^ 1> ICN;
+    const uint8_t* sA = bufA(cst);
+    const uint8_t* sB = bufB(cst);
+    const uint8_t* sAn = bufA(ICN{});
+    const uint8_t* sBn = bufB(ICN{});
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+      mfma_row(I0{}, mb);
+      if (mb < 4) read_b_frag(I1{}, sB, 1, mb);
+      read_a_frag(I1{}, sA, 1, mb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    has_next = issued > cs + 1;
+    if (has_next) {
+      wait_vmcnt<0>(); // this wave's copy of step cs+1 (and any older stores) landed
+      __syncthreads(); // every wave's; and every wave has read all of stage C
+      begin_copy();    // step cs + 2 into stage C
+    }
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+      mfma_row(I1{}, mb);
+      if (mb < 4) read_b_frag(I0{}, sBn, 0, mb); // stale but harmless without a next step
+      read_a_frag(I0{}, sAn, 0, mb);
+      if (mb == 0) copy_pair(cst, std::integral_constant<int, 0>{});
+      if (mb == 1) copy_pair(cst, std::integral_constant<int, 1>{});
+      if (mb == 2) copy_pair(cst, std::integral_constant<int, 2>{});
+      if (mb == 3) copy_pair(cst, std::integral_constant<int, 3>{});
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    publish_claim();
+    ++cs;
+  };
+  auto step = [&](auto cst) __attribute__((always_inline)) {
+    if constexpr (KSUB == 2) step_mid(cst); else step_top(cst);
   };
 
   // ---- the (tile, k-step) pipeline -----------------------------------------
-  begin_copy(); // step 0 into stage 0
-  copy_pair(I0{}, std::integral_constant<int, 0>{});
-  copy_pair(I0{}, std::integral_constant<int, 1>{});
-  copy_pair(I0{}, std::integral_constant<int, 2>{});
-  copy_pair(I0{}, std::integral_constant<int, 3>{});
-  publish_claim();
+  auto copy_whole = [&](auto c) __attribute__((always_inline)) {
+    begin_copy();
+    copy_pair(c, std::integral_constant<int, 0>{});
+    copy_pair(c, std::integral_constant<int, 1>{});
+    copy_pair(c, std::integral_constant<int, 2>{});
+    copy_pair(c, std::integral_constant<int, 3>{});
+  };
+  copy_whole(I0{}); // step 0 into stage 0
+  if constexpr (KSUB == 2) {
+    copy_whole(I1{}); // step 1 into stage 1 (nk >= 2: same tile)
+    publish_claim();
+    wait_vmcnt<L>();  // step 0's copy landed; step 1's may still fly
+    __syncthreads();
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) read_b_frag(I0{}, sB0, 0, nb);
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) read_a_frag(I0{}, sA0, 0, mb);
+  } else {
+    publish_claim();
+  }
   int c_q = 0; // consumer tile sequence number
   int c_tile = blockIdx.x;
   for (;;) {
@@ -424,7 +476,7 @@ __global__ void __launch_bounds__(THREADS) gemm_fast_kernel(Params p) {
       step(I0{});
       step(I1{});
     }
-    // tile finished: store it while the next tile's first copy is in flight
+    // tile finished: store it while the next tile's copies are in flight
     epilogue(c_tile);
     if (!has_next) break;
     c_tile = tile_of(++c_q);
