@@ -24,8 +24,8 @@
 //      fragments of k-group 1 are read from stage c;
 //   2. wait for this wave's copy of step s+1, one workgroup barrier: stage
 //      c^1 is complete, and every wave has read all of stage c;
-//   3. issue the copy of step s+2 into stage c, two instructions after each
-//      of the next four MFMA rows;
+//   3. issue the whole copy of step s+2 into stage c at once (eight 1 KiB
+//      instructions; measured faster than spreading them over MFMA rows);
 //   4. MFMAs of k-group 1 while the k-group-0 fragments of step s+1 are
 //      read from stage c^1.
 // So every LDS read has MFMAs to hide behind, and there is one barrier per
@@ -428,16 +428,16 @@ __global__ void __launch_bounds__(THREADS) gemm_fast_kernel(Params p) {
       wait_vmcnt<0>(); // this wave's copy of step cs+1 (and any older stores) landed
       __syncthreads(); // every wave's; and every wave has read all of stage C
       begin_copy();    // step cs + 2 into stage C
+      copy_pair(cst, std::integral_constant<int, 0>{});
+      copy_pair(cst, std::integral_constant<int, 1>{});
+      copy_pair(cst, std::integral_constant<int, 2>{});
+      copy_pair(cst, std::integral_constant<int, 3>{});
     }
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
       mfma_row(I1{}, mb);
       if (mb < 4) read_b_frag(I0{}, sBn, 0, mb); // stale but harmless without a next step
       read_a_frag(I0{}, sAn, 0, mb);
-      if (mb == 0) copy_pair(cst, std::integral_constant<int, 0>{});
-      if (mb == 1) copy_pair(cst, std::integral_constant<int, 1>{});
-      if (mb == 2) copy_pair(cst, std::integral_constant<int, 2>{});
-      if (mb == 3) copy_pair(cst, std::integral_constant<int, 3>{});
       __builtin_amdgcn_sched_barrier(0);
     }
     publish_claim();
