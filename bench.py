@@ -57,7 +57,60 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample duration")
     ap.add_argument("--modes", default=None, help="comma-separated subset of scheduling modes (0,1,2)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (reference for rocprof HBM counters)")
     return ap.parse_args()
+
+
+CSRC = os.path.join(ROOT, "persistent_tile_scheduling_macro_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_gemm_fast_f16_sweep4k.txt")
+
+
+def source_digest() -> str:
+    """sha256 over the kernel sources; HBM counters are only reported for the source they came from."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".h", ".hip")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str, workload: str):
+    """Calibrated HBM bytes per launch of `kernel` from the committed rocprofv3
+    summary, or None if there is none or the kernel source changed since."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+    except OSError:
+        return None
+    if kv.get("source_sha256") != source_digest() or kv.get("workload") != workload or kv.get("kernel") != kernel:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(mib: int) -> None:
+    """A plain device-to-device copy of known size: FETCH_SIZE and WRITE_SIZE of
+    this kernel give the scale from counter units to real bytes."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_launch": n * 4, "launches": 3}), flush=True)
 
 
 def problems(wl):
@@ -74,6 +127,9 @@ def problems(wl):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus_requested": args.gpus}))
@@ -173,10 +229,10 @@ def main():
     achieved = dom_flops / dom_time / 1e12
     kernel_names = {0: "gemm_fast_kernel<%s, kNonPersistent>", 1: "gemm_fast_kernel<%s, kStatic>",
                     2: "gemm_fast_kernel<%s, kDynamic>"}
+    kname = kernel_names[dom] % {"f16": "kF16", "bf16": "kBF16", "e4m3fn": "kF8E4M3"}[dtype]
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": None,
-                "kernel": kernel_names[dom] % {"f16": "kF16", "bf16": "kBF16", "e4m3fn": "kF8E4M3"}[dtype],
-                "launches": dom_n, "avg_us": round(dom_time / dom_n * 1e6, 2),
+                "frac": round(achieved / peak, 4), "traffic": measured_traffic(kname, args.workload),
+                "kernel": kname, "launches": dom_n, "avg_us": round(dom_time / dom_n * 1e6, 2),
                 "flops_per_launch_avg": dom_flops / dom_n}
 
     best = {}
@@ -231,13 +287,18 @@ def cpu_baseline(dtype, kind, wid, probs, seconds):
     m, n, K = max(seen, key=lambda x: x[2])
     A, B = si.operands(m, n, K, dtype, kind, workload=wid)
     Ab, Bb = si.bits(A), si.bits(B)
-    # calibrate on a few rows, then size the sample to about `seconds`
-    rows = np.arange(0, m, max(1, m // 16))[:16]
-    t0 = time.perf_counter()
-    oracle.gemm(Ab, Bb, dtype, rows=rows, nthreads=cores)
-    t_cal = time.perf_counter() - t0
-    per_row = t_cal / len(rows)
-    nrows = int(min(m, max(len(rows), seconds / max(per_row, 1e-9))))
+    # Each call decodes all of B once before the row loop, so time two row
+    # counts and size the sample from the per-row slope to take about `seconds`.
+    def timed(r):
+        t0 = time.perf_counter()
+        oracle.gemm(Ab, Bb, dtype, rows=np.arange(r) * (m // r), nthreads=cores)
+        return time.perf_counter() - t0
+
+    r1, r2 = 16, 64
+    t1, t2 = timed(r1), timed(r2)
+    per_row = max((t2 - t1) / (r2 - r1), t2 / r2 / 4, 1e-9)
+    fixed = max(t1 - r1 * per_row, 0.0)
+    nrows = int(min(m, max(r2, (seconds - fixed) / per_row)))
     rng = np.random.default_rng(0)
     sample = np.sort(rng.choice(m, size=nrows, replace=False))
     t0 = time.perf_counter()
