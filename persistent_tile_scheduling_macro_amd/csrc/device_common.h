@@ -116,7 +116,8 @@ __host__ __device__ inline void tile_coords(int t, const Params& p, int* pm, int
 // A counter value outside [0, T) cannot come from this protocol; it is
 // treated as a failed claim so a corrupted counter can never index a tile
 // outside the grid.
-__device__ inline int claim_tile(int* counter, int T, int G) {
+// Host-callable too, so that a CPU test can race it from many threads.
+__host__ __device__ inline int claim_tile(int* counter, int T, int G) {
   int c = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (c == T - 1) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return (c < 0 || c >= T) ? T : c + G;
