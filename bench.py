@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample duration")
     ap.add_argument("--modes", default=None, help="comma-separated subset of scheduling modes (0,1,2)")
+    ap.add_argument("--tile", default="auto", choices=["auto", "256", "128"],
+                    help="macro tile of the fast kernel (auto: the library's default choice)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (reference for rocprof HBM counters)")
     return ap.parse_args()
@@ -169,6 +171,8 @@ def main():
     stream = torch.cuda.current_stream(dev)
     h = pg.pgemm_create(0)
     pg.pgemm_set_stream(h, stream)
+    pg.pgemm_set_tile_config(h, {"auto": pg.PGEMM_TILE_AUTO, "256": pg.PGEMM_TILE_256,
+                                 "128": pg.PGEMM_TILE_128}[args.tile])
 
     def launch(p):
         m, n, K, mode, gm = p
@@ -214,22 +218,30 @@ def main():
                       "us": round(t * 1e6, 2), "tflops": round(flops[p] / t / 1e12, 1),
                       "frac_peak": round(flops[p] / t / 1e12 / peak, 4),
                       "frac_roofline": round(flops[p] / t / 1e12 / min(peak, flops[p] / byts * HBM_GBS / 1e3), 4),
-                      "tiles": info["tiles"], "grid": info["grid"],
+                      "tile": f'{info["bm"]}x{info["bn"]}', "tiles": info["tiles"], "grid": info["grid"],
                       "tiles_per_wg": round(info["tiles"] / info["grid"], 2)})
 
-    # roofline of the dominant kernel (most total time among the three mode kernels)
+    # roofline of the dominant kernel: the (scheduling mode, macro tile) instance with the
+    # most total time
+    body = {}
+    for p in probs:
+        info = pg.pgemm_query_launch(h, p[0], p[1], p[2], dt_code, p[3], p[4])
+        body[p] = (p[3], info["bm"] if info["fast_path"] else 0)
     tot = {}
     for p in probs:
-        tot.setdefault(p[3], [0.0, 0.0, 0])
-        tot[p[3]][0] += sum(per[p])
-        tot[p[3]][1] += flops[p] * len(per[p])
-        tot[p[3]][2] += len(per[p])
+        tot.setdefault(body[p], [0.0, 0.0, 0])
+        tot[body[p]][0] += sum(per[p])
+        tot[body[p]][1] += flops[p] * len(per[p])
+        tot[body[p]][2] += len(per[p])
     dom = max(tot, key=lambda k: tot[k][0])
     dom_time, dom_flops, dom_n = tot[dom]
     achieved = dom_flops / dom_time / 1e12
-    kernel_names = {0: "gemm_fast_kernel<%s, kNonPersistent>", 1: "gemm_fast_kernel<%s, kStatic>",
-                    2: "gemm_fast_kernel<%s, kDynamic>"}
-    kname = kernel_names[dom] % {"f16": "kF16", "bf16": "kBF16", "e4m3fn": "kF8E4M3"}[dtype]
+    sched_names = {0: "kNonPersistent", 1: "kStatic", 2: "kDynamic"}
+    dt_name = {"f16": "kF16", "bf16": "kBF16", "e4m3fn": "kF8E4M3"}[dtype]
+    if dom[1]:
+        kname = f"gemm_fast_kernel<{dt_name}, {sched_names[dom[0]]}, kTile{dom[1]}>"
+    else:
+        kname = f"gemm_generic_kernel<{dt_name}, {sched_names[dom[0]]}>"
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": measured_traffic(kname, args.workload),
                 "kernel": kname, "launches": dom_n, "avg_us": round(dom_time / dom_n * 1e6, 2),
@@ -256,7 +268,7 @@ def main():
         "value": round(value, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(wall / args.steps * 1e3, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": dtype if dtype != "e4m3fn" else "e4m3fn->bf16", "data": "synthetic",
-        "config": {"workload": desc, "name": args.workload, "launches_per_step": len(probs),
+        "config": {"workload": desc, "name": args.workload, "tile": args.tile, "launches_per_step": len(probs),
                    "flops_per_step": step_flops},
         "frac_of_peak": round(value / peak, 4),
         "mode_tflops": mode_tflops,

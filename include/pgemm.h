@@ -71,6 +71,22 @@ typedef enum {
   PGEMM_SCHED_DYNAMIC = 2
 } pgemm_sched_t;
 
+/* Macro-tile configurations of the fast kernel (the Triton persistent-
+ * matmul issue tunes BLOCK_SIZE_M/N per problem, "What I've tried").
+ * TILE_256: 256 x 256 tiles, 512 threads, one workgroup per CU: the fewest
+ *   operand bytes per flop, for problems with many tiles.
+ * TILE_128: 128 x 128 tiles, 256 threads, two workgroups per CU: four times
+ *   the tiles, so small problems fill the chip and persistent workgroups
+ *   get several tiles each.
+ * AUTO (default): TILE_128 when 256 x 256 tiles would number fewer than the
+ *   CUs (some CUs would idle), else TILE_256. The environment variable PGEMM_TILE (256 or 128)
+ *   overrides the default at pgemm_create. */
+typedef enum {
+  PGEMM_TILE_AUTO = 0,
+  PGEMM_TILE_256 = 1,
+  PGEMM_TILE_128 = 2
+} pgemm_tile_t;
+
 /* Create a handle on HIP device `device` (which becomes current). Allocates
  * the dynamic scheduler's device work counter (zeroed) and caches the CU
  * count. The handle starts on the null stream. *out is NULL on failure. */
@@ -96,8 +112,9 @@ int pgemm_set_stream(pgemm_handle_t h, void* hip_stream);
  *     another, so that stays correct. G is clamped to the tile count T.
  * Operands whose K and N are multiples of 16 bytes of elements (8 for
  * fp16/bf16, 16 for fp8) with 16-byte-aligned A, B and 8-byte-aligned C
- * take the fast 256 x 256 tile kernel; others take a generic 64 x 64 tile
- * kernel with the same schedulers (correct, slower). */
+ * take the fast kernel (256 x 256 or 128 x 128 tiles, pgemm_tile_t);
+ * others take a generic 64 x 64 tile kernel with the same schedulers
+ * (correct, slower). */
 int pgemm_run(pgemm_handle_t h, const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
               int dtype, int sched_mode, int grid_multiple);
 
@@ -141,6 +158,11 @@ int pgemm_query_launch(pgemm_handle_t h, int64_t M, int64_t N, int64_t K, int dt
  * environment variables PGEMM_GROUP_M and PGEMM_XCD_REMAP override the
  * defaults at pgemm_create. */
 int pgemm_set_tile_order(pgemm_handle_t h, int group_m, int xcd_remap);
+
+/* Choose the fast kernel's macro tile for later runs on this handle
+ * (pgemm_tile_t). Unaligned operands always take the generic 64 x 64 body.
+ * Returns PGEMM_ERR_INVALID_ARG for an unknown value. */
+int pgemm_set_tile_config(pgemm_handle_t h, int tile);
 
 /* Host mirror of the device tile order: (pid_m, pid_n) of tile t for an
  * n_m x n_n tile grid, with the same knobs and CU-count chunking the

@@ -28,6 +28,10 @@ PGEMM_SCHED_NONPERSISTENT = 0
 PGEMM_SCHED_STATIC = 1
 PGEMM_SCHED_DYNAMIC = 2
 
+PGEMM_TILE_AUTO = 0
+PGEMM_TILE_256 = 1
+PGEMM_TILE_128 = 2
+
 DTYPE_NAMES = {"f16": PGEMM_F16, "bf16": PGEMM_BF16, "e4m3fn": PGEMM_F8E4M3_BF16}
 SCHED_NAMES = {"nonpersistent": PGEMM_SCHED_NONPERSISTENT, "static": PGEMM_SCHED_STATIC,
                "dynamic": PGEMM_SCHED_DYNAMIC}
@@ -59,6 +63,7 @@ _set_owner_log = _sig("pgemm_set_owner_log", _int, _vp, _vp, _i64)
 _query_launch = _sig("pgemm_query_launch", _int, _vp, _i64, _i64, _i64, _int, _int, _int,
                      _ip, _ip, _ip, _ip, _ip, _ip, _ip)
 _set_tile_order = _sig("pgemm_set_tile_order", _int, _vp, _int, _int)
+_set_tile_config = _sig("pgemm_set_tile_config", _int, _vp, _int)
 _tile_coords = _sig("pgemm_tile_coords", _int, _i64, _i64, _i64, _int, _int, _ip, _ip)
 _read_work_counter = _sig("pgemm_read_work_counter", _int, _vp, ctypes.POINTER(_i32))
 
@@ -139,6 +144,10 @@ def pgemm_query_launch(h, M: int, N: int, K: int, dtype: int, sched_mode: int, g
 
 def pgemm_set_tile_order(h, group_m: int = 8, xcd_remap: bool = True) -> None:
     _check(_set_tile_order(h, int(group_m), int(bool(xcd_remap))), h)
+
+
+def pgemm_set_tile_config(h, tile: int) -> None:
+    _check(_set_tile_config(h, int(tile)), h)
 
 
 def pgemm_tile_coords(t: int, n_m: int, n_n: int, group_m: int = 8, cu_chunk: int = 0):

@@ -1,15 +1,22 @@
 // The fast GEMM kernel for aligned operands (K and N multiples of 16 bytes
-// of elements, 16-byte aligned A and B).
+// of elements, 16-byte aligned A and B), in two macro-tile configurations:
 //
-// Macro tile 256 x 256, 512 threads = 8 waves (two per SIMD) in a 2 x 4
-// arrangement, each wave owning a 128 x 64 sub-tile (8 x 4 blocks of
-// 16 x 16 MFMA outputs, 128 fp32 accumulators per lane, kept in AGPRs).
+//   kTile256: 256 x 256 tile, 512 threads = 8 waves (two per SIMD) in a
+//             2 x 4 arrangement, each wave owning a 128 x 64 sub-tile
+//             (8 x 4 blocks of 16 x 16 MFMA outputs, 128 fp32 accumulators
+//             per lane, kept in AGPRs); one workgroup per CU.
+//   kTile128: 128 x 128 tile, 256 threads = 4 waves in 2 x 2, each wave
+//             owning a 64 x 64 sub-tile (4 x 4 blocks, 64 accumulators);
+//             two workgroups per CU, so a problem has four times the tiles
+//             (a 4096 x 4096 C has 1024, two per persistent workgroup).
+//
 // K is consumed in steps of 128 bytes of elements (BK = 64 for fp16/bf16,
-// 128 for fp8). Each step's A (256 x BK) and B (BK x 256) slices are
-// copied global -> LDS by buffer loads that write LDS directly (no register
+// 128 for fp8). Each step's A (BM x BK) and B (BK x BN) slices are copied
+// global -> LDS by buffer loads that write LDS directly (no register
 // staging) into a two-stage ring, so the copy of step s+1 overlaps the
 // MFMAs of step s (the copy/compute overlap of the persistent-kernel forum
-// thread, first answer).
+// thread, first answer). Both configurations copy 4 + 4 KiB-sized
+// instructions per thread per step.
 //
 // Why this shape on gfx950 (measured on the part, not taken from the
 // pages): the CU's global -> LDS path moves about 30 B/clk, while a 256 x
@@ -47,13 +54,14 @@
 // bank-conflict-free on gfx950 (measured: 64 banks; ds_read_b128 serves
 // lanes {0-7,16-23}, {8-15,24-31}, ... per pass; transpose reads serve 32
 // lanes per pass):
-//   A, 16-bit: 256 rows (m) x 128 B; chunk c of row r at c ^ (r & 7).
-//   A, fp8:    256 rows (m) x 128 B; chunk c of row r at c ^ sa8(r),
+//   A, 16-bit: BM rows (m) x 128 B; chunk c of row r at c ^ (r & 7).
+//   A, fp8:    BM rows (m) x 128 B; chunk c of row r at c ^ sa8(r),
 //              sa8(r) = ((r >> 1) & 1) | (r & 4).
-//   B, 16-bit: 64 rows (k) x 512 B; chunk c of row r at
+//   B, 16-bit: 64 rows (k) x 2*BN B; chunk c of row r at
 //              c ^ (2*(r & 3) + 8*((r >> 3) & 1)).
-//   B, fp8:    128 rows (k) x 256 B; chunk c of row r at
-//              c ^ ((r & 7) + 8*((r >> 5) & 1)).
+//   B, fp8:    128 rows (k) x BN B; chunk c of row r at
+//              c ^ ((r & 7) + 8*((r >> 5) & 1))          (BN = 256)
+//              c ^ (((r >> 1) & 3) + 4*((r >> 5) & 1))   (BN = 128).
 // A fragments are plain 16-byte reads of consecutive k. B is n-contiguous
 // in memory, so its fragments come from the gfx950 LDS transpose reads
 // (ds_read_b64_tr_b16 / _b8), which hand each lane one column's
@@ -68,10 +76,27 @@
 namespace pgemm {
 namespace fast {
 
-constexpr int BM = 256, BN = 256, THREADS = 512;
-constexpr int WAVES = THREADS / 64;
-
 __host__ __device__ constexpr int block_k(int esize) { return 128 / esize; }
+
+enum TileConfig : int { kTile256 = 0, kTile128 = 1 };
+
+template <int CFG>
+struct Tile;
+template <>
+struct Tile<kTile256> {
+  static constexpr int BM = 256, BN = 256, WAVES = 8, WGM = 2, WGN = 4;
+};
+template <>
+struct Tile<kTile128> {
+  static constexpr int BM = 128, BN = 128, WAVES = 4, WGM = 2, WGN = 2;
+};
+
+// Swizzle of B's LDS rows: row k's chunk c is stored at chunk c ^ b_swz(k).
+template <int ES, int B_ROW>
+__host__ __device__ constexpr int b_swz(int k) {
+  return ES == 2 ? 2 * (k & 3) + 8 * ((k >> 3) & 1)
+                 : (B_ROW == 256 ? (k & 7) + 8 * ((k >> 5) & 1) : ((k >> 1) & 3) + 4 * ((k >> 5) & 1));
+}
 
 template <int DT>
 struct Frag;
@@ -91,21 +116,21 @@ __device__ inline void wait_vmcnt() {
 
 // Read the B fragment of one 16-column block: lane (16g + s) ends up with
 // column s of the block and the k values its A partner holds.
-template <int DT>
+template <int DT, int B_ROW>
 __device__ inline typename Frag<DT>::t read_b(const uint8_t* base) {
   if constexpr (Traits<DT>::esize == 2) {
     // two transpose reads: k rows +0..3 and +4..7 of the lane group's 8 k
     fp16x4_raw_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16(PGEMM_LDS(fp16x4_raw_t, base));
-    fp16x4_raw_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16(PGEMM_LDS(fp16x4_raw_t, base + 4 * 512));
+    fp16x4_raw_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16(PGEMM_LDS(fp16x4_raw_t, base + 4 * B_ROW));
     intx2_t l = __builtin_bit_cast(intx2_t, lo), h = __builtin_bit_cast(intx2_t, hi);
     intx4_t w = {l[0], l[1], h[0], h[1]};
     return __builtin_bit_cast(typename Frag<DT>::t, w);
   } else {
     // four transpose reads of 8 k each (k rows +0, +8, +16, +24)
     intx2_t r0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(PGEMM_LDS(intx2_t, base));
-    intx2_t r1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(PGEMM_LDS(intx2_t, base + 8 * 256));
-    intx2_t r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(PGEMM_LDS(intx2_t, base + 16 * 256));
-    intx2_t r3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(PGEMM_LDS(intx2_t, base + 24 * 256));
+    intx2_t r1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(PGEMM_LDS(intx2_t, base + 8 * B_ROW));
+    intx2_t r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(PGEMM_LDS(intx2_t, base + 16 * B_ROW));
+    intx2_t r3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(PGEMM_LDS(intx2_t, base + 24 * B_ROW));
     return intx8_t{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
   }
 }
@@ -121,18 +146,27 @@ __device__ inline typename Frag<DT>::t read_a(const uint8_t* lo, const uint8_t* 
   }
 }
 
-template <int DT, int SCHED>
-__global__ void __launch_bounds__(THREADS) gemm_fast_kernel(Params p) {
+template <int DT, int SCHED, int CFG>
+__global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, 2) gemm_fast_kernel(Params p) {
+  constexpr int BM = Tile<CFG>::BM, BN = Tile<CFG>::BN;
+  constexpr int WAVES = Tile<CFG>::WAVES, THREADS = WAVES * 64;
+  constexpr int WGN = Tile<CFG>::WGN;             // waves along n
+  constexpr int WTM = BM / Tile<CFG>::WGM;        // rows of a wave's sub-tile
+  constexpr int MB = WTM / 16;                    // 16-row MFMA blocks per wave (8 or 4)
+  static_assert(BN / WGN == 64, "each wave owns 64 columns = 4 MFMA blocks");
   constexpr int ES = Traits<DT>::esize;
   constexpr int BK = block_k(ES);                // k elements per step
   constexpr int KSUB = BK / Traits<DT>::kgroup;  // MFMA k-groups per step (2 or 1)
   constexpr int A_ROW = 128;                     // bytes per A row in LDS
-  constexpr int A_BYTES = BM * A_ROW;            // 32 KiB per stage
-  constexpr int B_ROW = BN * ES;                 // bytes per B row in LDS (512 or 256)
-  constexpr int B_BYTES = BK * B_ROW;            // 32 KiB per stage
+  constexpr int A_BYTES = BM * A_ROW;            // 32 or 16 KiB per stage
+  constexpr int B_ROW = BN * ES;                 // bytes per B row in LDS (512, 256 or 128)
+  constexpr int B_BYTES = BK * B_ROW;            // 32 or 16 KiB per stage
+  constexpr int B_CPR = B_ROW / 16;              // 16-byte chunks per B row
+  constexpr int B_RPI = 1024 / B_ROW;            // B rows per 1 KiB copy instruction
   constexpr int LA = A_BYTES / (THREADS * 16), LB = B_BYTES / (THREADS * 16);
   constexpr int L = LA + LB;                     // copy instructions per thread per step
   static_assert(LA == 4 && LB == 4, "copy split assumes 4 + 4 instructions per step");
+  static_assert(MB <= 8, "fragment arrays sized for at most 8 row blocks");
   typedef typename Traits<DT>::out_t out_t;
   typedef typename Frag<DT>::t frag_t;
   typedef std::integral_constant<int, 0> I0;
@@ -154,7 +188,7 @@ __global__ void __launch_bounds__(THREADS) gemm_fast_kernel(Params p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // wave-uniform, lives in an SGPR
-  const int wm = wave >> 2, wn = wave & 3;                   // 2 x 4 waves of 128 x 64
+  const int wm = wave / WGN, wn = wave % WGN;                // WGM x WGN waves of WTM x 64
   const int M = p.M, N = p.N, K = p.K, T = p.T, G = p.G;
   // k-steps per tile, rounded up to even so that every tile starts on stage
   // 0 (an extra step reads zeros: it lies past K)
@@ -164,11 +198,14 @@ __global__ void __launch_bounds__(THREADS) gemm_fast_kernel(Params p) {
   const int64_t ldc = N;               // elements per row of C
 
   // ---- per-lane constants of the global -> LDS copy ------------------------
-  // Instruction q = wave + 8j fills one 1 KiB block of a stage: A rows
+  // Instruction q = wave + WAVES*j fills one 1 KiB block of a stage: A rows
   // 8q..8q+7 (lane -> row 8q + lane/8, physical chunk lane % 8); B rows
-  // 2q, 2q+1 (16-bit) or 4q..4q+3 (fp8). The swizzles depend on row bits
-  // that are constant per lane and wave (fp8 B: and on the parity of j).
-  const int a_row0 = 8 * wave + (lane >> 3); // + 64 j
+  // B_RPI*q .. B_RPI*q + B_RPI-1 (lane -> row B_RPI*q + lane/B_CPR, physical
+  // chunk lane % B_CPR). Each lane fetches the global chunk that the swizzle
+  // stores at its physical position (the swizzles are XOR involutions). They
+  // depend on row bits that are constant per lane and wave, and for fp8 B
+  // also on the parity of j.
+  const int a_row0 = 8 * wave + (lane >> 3); // + 8*WAVES j
   int a_chunk;
   if constexpr (ES == 2) {
     a_chunk = (lane & 7) ^ (lane >> 3);
@@ -176,24 +213,15 @@ __global__ void __launch_bounds__(THREADS) gemm_fast_kernel(Params p) {
     const int r = lane >> 3;
     a_chunk = (lane & 7) ^ (((r >> 1) & 1) | (r & 4));
   }
-  int b_row0, b_chunk0, b_chunk1;
-  if constexpr (ES == 2) {
-    b_row0 = 2 * wave + (lane >> 5); // + 16 j
-    const int h = 2 * (b_row0 & 3) + 8 * ((wave >> 2) & 1);
-    b_chunk0 = (lane & 31) ^ h;
-    b_chunk1 = b_chunk0;
-  } else {
-    b_row0 = 4 * wave + (lane >> 4); // + 32 j
-    const int h = b_row0 & 7;        // + 8 for odd j
-    b_chunk0 = (lane & 15) ^ h;
-    b_chunk1 = (lane & 15) ^ (h + 8);
-  }
+  const int b_row0 = B_RPI * wave + lane / B_CPR; // + B_RPI*WAVES j
+  const int b_chunk0 = (lane % B_CPR) ^ b_swz<ES, B_ROW>(b_row0);
+  const int b_chunk1 = (lane % B_CPR) ^ b_swz<ES, B_ROW>(b_row0 + B_RPI * WAVES);
 
   // ---- per-lane constants of the fragment reads ----------------------------
   const int g = lane >> 4, s16 = lane & 15;
   int a_off[KSUB][2];
   {
-    const int r = wm * 128 + s16; // + mb * 16
+    const int r = wm * WTM + s16; // + mb * 16
 #pragma unroll
     for (int kk = 0; kk < KSUB; ++kk) {
       if constexpr (ES == 2) {
@@ -209,16 +237,16 @@ __global__ void __launch_bounds__(THREADS) gemm_fast_kernel(Params p) {
   int b_off[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
+    // the swizzle is the same for every row this lane reads from here
+    // (+4 and +32 rows for 16-bit, +8/+16/+24 for fp8)
     if constexpr (ES == 2) {
-      const int k = 8 * g + (s16 >> 2); // + 32 kk, +4 for the second read
+      const int k = 8 * g + (s16 >> 2);
       const int Lc = wn * 8 + 2 * nb + ((s16 & 3) >> 1);
-      const int h = 2 * (s16 >> 2) + 8 * (g & 1);
-      b_off[nb] = k * B_ROW + 16 * (Lc ^ h) + 8 * (s16 & 1);
+      b_off[nb] = k * B_ROW + 16 * (Lc ^ b_swz<ES, B_ROW>(k)) + 8 * (s16 & 1);
     } else {
-      const int k = 32 * g + (s16 >> 1); // +8, +16, +24 for reads 1..3
+      const int k = 32 * g + (s16 >> 1);
       const int Lc = wn * 4 + nb;
-      const int h = (s16 >> 1) + 8 * (g & 1);
-      b_off[nb] = k * B_ROW + 16 * (Lc ^ h) + 8 * (s16 & 1);
+      b_off[nb] = k * B_ROW + 16 * (Lc ^ b_swz<ES, B_ROW>(k)) + 8 * (s16 & 1);
     }
   }
 
@@ -295,19 +323,13 @@ __global__ void __launch_bounds__(THREADS) gemm_fast_kernel(Params p) {
     constexpr int J = decltype(jc)::value;
     if (!p_busy) return;
     if constexpr (J < LA) {
-      const bool ok = p_kval & (a_row0 + 64 * J < p_mrem);
-      const uint32_t off = ok ? a_base + (uint32_t)(64 * J) * (uint32_t)lda : kOOB;
+      const bool ok = p_kval & (a_row0 + 8 * WAVES * J < p_mrem);
+      const uint32_t off = ok ? a_base + (uint32_t)(8 * WAVES * J) * (uint32_t)lda : kOOB;
       load16_to_lds(ra, sA + (wave + WAVES * J) * 1024, off);
     } else {
       constexpr int JB = J - LA;
-      int row, Lc;
-      if constexpr (ES == 2) {
-        row = b_row0 + 16 * JB;
-        Lc = b_chunk0;
-      } else {
-        row = b_row0 + 32 * JB;
-        Lc = (JB & 1) ? b_chunk1 : b_chunk0;
-      }
+      const int row = b_row0 + B_RPI * WAVES * JB;
+      const int Lc = (JB & 1) ? b_chunk1 : b_chunk0;
       const bool ok = (row < p_krem) & (16 * Lc < p_nrem);
       const uint32_t off = ok ? (uint32_t)row * (uint32_t)ldb + 16u * (uint32_t)Lc : kOOB;
       load16_to_lds(rb, sB + (wave + WAVES * JB) * 1024, off);
@@ -321,11 +343,11 @@ __global__ void __launch_bounds__(THREADS) gemm_fast_kernel(Params p) {
   };
 
   // ---- accumulators and fragments -------------------------------------------
-  floatx4_t acc[8][4];
-  frag_t af[2][8], bf[2][4];
+  floatx4_t acc[MB][4];
+  frag_t af[2][MB], bf[2][4];
   auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
     acc_drain(); // accvgpr writes -> MFMA srcC reads
@@ -336,7 +358,7 @@ __global__ void __launch_bounds__(THREADS) gemm_fast_kernel(Params p) {
   };
   auto read_b_frag = [&](auto f, const uint8_t* sB, int kk, int nb) __attribute__((always_inline)) {
     constexpr int F = decltype(f)::value;
-    bf[F][nb] = read_b<DT>(sB + b_off[nb] + kk * 32 * B_ROW);
+    bf[F][nb] = read_b<DT, B_ROW>(sB + b_off[nb] + kk * 32 * B_ROW);
   };
   auto mfma_row = [&](auto f, int mb) __attribute__((always_inline)) {
     constexpr int F = decltype(f)::value;
@@ -349,11 +371,11 @@ __global__ void __launch_bounds__(THREADS) gemm_fast_kernel(Params p) {
     acc_drain();
     int pm, pn;
     tile_coords(tile, p, &pm, &pn);
-    const int mrow = pm * BM + wm * 128 + s16;
+    const int mrow = pm * BM + wm * WTM + s16;
     const int ncol = pn * BN + wn * 64 + 4 * g;
     out_t* C = reinterpret_cast<out_t*>(p.C);
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
+    for (int mb = 0; mb < MB; ++mb) {
       const int m = mrow + mb * 16;
       if (m < M) {
 #pragma unroll
@@ -392,9 +414,9 @@ __global__ void __launch_bounds__(THREADS) gemm_fast_kernel(Params p) {
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) read_b_frag(I0{}, sB, 0, nb);
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) read_a_frag(I0{}, sA, 0, mb);
+    for (int mb = 0; mb < MB; ++mb) read_a_frag(I0{}, sA, 0, mb);
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
+    for (int mb = 0; mb < MB; ++mb) {
       mfma_row(I0{}, mb);
       if (mb == 0) copy_pair(ICN{}, std::integral_constant<int, 0>{});
       if (mb == 1) copy_pair(ICN{}, std::integral_constant<int, 1>{});
@@ -417,7 +439,7 @@ __global__ void __launch_bounds__(THREADS) gemm_fast_kernel(Params p) {
     const uint8_t* sAn = bufA(ICN{});
     const uint8_t* sBn = bufB(ICN{});
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
+    for (int mb = 0; mb < MB; ++mb) {
       mfma_row(I0{}, mb);
       if (mb < 4) read_b_frag(I1{}, sB, 1, mb);
       read_a_frag(I1{}, sA, 1, mb);
@@ -434,7 +456,7 @@ __global__ void __launch_bounds__(THREADS) gemm_fast_kernel(Params p) {
       copy_pair(cst, std::integral_constant<int, 3>{});
     }
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
+    for (int mb = 0; mb < MB; ++mb) {
       mfma_row(I1{}, mb);
       if (mb < 4) read_b_frag(I0{}, sBn, 0, mb); // stale but harmless without a next step
       read_a_frag(I0{}, sAn, 0, mb);
@@ -464,7 +486,7 @@ __global__ void __launch_bounds__(THREADS) gemm_fast_kernel(Params p) {
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) read_b_frag(I0{}, sB0, 0, nb);
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) read_a_frag(I0{}, sA0, 0, mb);
+    for (int mb = 0; mb < MB; ++mb) read_a_frag(I0{}, sA0, 0, mb);
   } else {
     publish_claim();
   }

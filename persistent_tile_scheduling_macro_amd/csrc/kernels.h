@@ -7,10 +7,14 @@ namespace pgemm {
 
 typedef void (*kernel_fn)(Params);
 
-// Returns the kernel for (scheduling mode, fast or generic body).
-kernel_fn pick_kernel_f16(int sched, bool fast);
-kernel_fn pick_kernel_bf16(int sched, bool fast);
-kernel_fn pick_kernel_f8(int sched, bool fast);
+// Tile body of a launch: the fast kernel in one of its two macro-tile
+// configurations, or the generic 64 x 64 body for unaligned operands.
+enum Body : int { kBodyGeneric = 0, kBodyTile256 = 1, kBodyTile128 = 2 };
+
+// Returns the kernel for (scheduling mode, tile body).
+kernel_fn pick_kernel_f16(int sched, int body);
+kernel_fn pick_kernel_bf16(int sched, int body);
+kernel_fn pick_kernel_f8(int sched, int body);
 
 // K == 0: C = 0 (an empty sum). n = M * N output elements.
 void launch_fill_zero(void* C, int64_t n, hipStream_t stream);

@@ -1,20 +1,9 @@
 // Instantiations of the GEMM kernels for one element type.
-#include "gemm_fast.h"
-#include "gemm_generic.h"
-#include "kernels.h"
+#include "kernels_impl.h"
 
 namespace pgemm {
 
-kernel_fn pick_kernel_f16(int sched, bool fast) {
-  switch (sched) {
-    case kNonPersistent:
-      return fast ? fast::gemm_fast_kernel<kF16, kNonPersistent> : generic::gemm_generic_kernel<kF16, kNonPersistent>;
-    case kStatic:
-      return fast ? fast::gemm_fast_kernel<kF16, kStatic> : generic::gemm_generic_kernel<kF16, kStatic>;
-    default:
-      return fast ? fast::gemm_fast_kernel<kF16, kDynamic> : generic::gemm_generic_kernel<kF16, kDynamic>;
-  }
-}
+kernel_fn pick_kernel_f16(int sched, int body) { return pick_for_dtype<kF16>(sched, body); }
 
 } // namespace pgemm
 

@@ -1,0 +1,29 @@
+// Instantiation of every (scheduling mode, tile body) kernel of one element
+// type; included by that type's translation unit only.
+#pragma once
+
+#include "gemm_fast.h"
+#include "gemm_generic.h"
+#include "kernels.h"
+
+namespace pgemm {
+
+template <int DT, int SCHED>
+kernel_fn pick_body(int body) {
+  switch (body) {
+    case kBodyTile256: return fast::gemm_fast_kernel<DT, SCHED, fast::kTile256>;
+    case kBodyTile128: return fast::gemm_fast_kernel<DT, SCHED, fast::kTile128>;
+    default: return generic::gemm_generic_kernel<DT, SCHED>;
+  }
+}
+
+template <int DT>
+kernel_fn pick_for_dtype(int sched, int body) {
+  switch (sched) {
+    case kNonPersistent: return pick_body<DT, kNonPersistent>(body);
+    case kStatic: return pick_body<DT, kStatic>(body);
+    default: return pick_body<DT, kDynamic>(body);
+  }
+}
+
+} // namespace pgemm

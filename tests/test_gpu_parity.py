@@ -8,6 +8,9 @@ Checks, per case (see the oracle's header for what is computed):
   any order);
 * tile-visit counter: every output tile written exactly once;
 * C bitwise identical across the three modes (one tile body).
+
+Every case runs with each macro-tile configuration of the fast kernel
+(256 x 256 and 128 x 128), selected explicitly through the C ABI.
 """
 import numpy as np
 import pytest
@@ -22,6 +25,7 @@ DT = {"f16": 0, "bf16": 1, "e4m3fn": 2}
 OUT = {"f16": ("f16", torch.float16), "bf16": ("bf16", torch.bfloat16), "e4m3fn": ("bf16", torch.bfloat16)}
 TOL = {"f16": 2e-3, "bf16": 2e-3, "e4m3fn": 1e-2}
 MODES = [0, 1, 2]
+TILES = {"t256": 1, "t128": 2}  # PGEMM_TILE_256, PGEMM_TILE_128
 
 
 @pytest.fixture(scope="module")
@@ -32,9 +36,10 @@ def pg():
     return pg
 
 
-@pytest.fixture(scope="module")
-def handle(pg):
+@pytest.fixture(scope="module", params=sorted(TILES))
+def handle(pg, request):
     h = pg.pgemm_create(0)
+    pg.pgemm_set_tile_config(h, TILES[request.param])
     yield h
     pg.pgemm_destroy(h)
 
@@ -74,7 +79,7 @@ def test_workload_256_all_modes(pg, handle, dtype):
         c, v, info = run(pg, handle, A, B, dtype, mode)
         err = oracle.normwise_error(c, OUT[dtype][0], ref)
         assert err <= TOL[dtype], (mode, err)
-        assert info["fast_path"] == 1 and info["tiles"] == 1
+        assert info["fast_path"] == 1 and info["tiles"] == (256 // info["bm"]) ** 2
         assert np.array_equal(v, np.ones_like(v)), v
         outs.append(c)
     for o in outs[1:]:
@@ -137,7 +142,7 @@ def test_static_owner_map_and_dynamic_counter(pg, handle):
     """Static: owner[t] = t mod G (deterministic mapping). Dynamic: every tile once,
     the work counter back at 0 after each launch, also back to back."""
     dev = torch.device("cuda:0")
-    M, N, K = 8192, 4096, 64  # 32 x 16 = 512 tiles of 256 x 256
+    M, N, K = 8192, 4096, 64  # 512 tiles of 256 x 256 or 2048 of 128 x 128
     A, B = si.operands(M, N, K, "f16", "small_int", workload=3)
     want = oracle.round_to(oracle.gemm(si.bits(A), si.bits(B), "f16"), "f16")
     Ad, Bd = A.to(dev), B.to(dev)
