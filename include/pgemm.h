@@ -111,7 +111,7 @@ int pgemm_set_stream(pgemm_handle_t h, void* hip_stream);
  *     comment), which may exceed co-residency -- no workgroup waits on
  *     another, so that stays correct. G is clamped to the tile count T.
  * Operands whose K and N are multiples of 16 bytes of elements (8 for
- * fp16/bf16, 16 for fp8) with 16-byte-aligned A, B and 8-byte-aligned C
+ * fp16/bf16, 16 for fp8) with 16-byte-aligned A, B and C
  * take the fast kernel (256 x 256 or 128 x 128 tiles, pgemm_tile_t);
  * others take a generic 64 x 64 tile kernel with the same schedulers
  * (correct, slower). */

@@ -191,4 +191,24 @@ __device__ inline void store4(OutT* dst, floatx4_t v) {
   *reinterpret_cast<v4*>(dst) = o;
 }
 
+// Eight consecutive outputs from two 4-wide accumulator blocks: a's values
+// first, or b's first when `swap`; one 16-byte store (dst 16-byte aligned).
+template <class OutT>
+__device__ inline void store8(OutT* dst, floatx4_t a, floatx4_t b, bool swap) {
+  typedef OutT v4 __attribute__((ext_vector_type(4)));
+  v4 oa, ob;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    oa[e] = to_out(a[e], (OutT*)nullptr);
+    ob[e] = to_out(b[e], (OutT*)nullptr);
+  }
+  const intx2_t wa = __builtin_bit_cast(intx2_t, oa), wb = __builtin_bit_cast(intx2_t, ob);
+  intx4_t w;
+  w[0] = swap ? wb[0] : wa[0];
+  w[1] = swap ? wb[1] : wa[1];
+  w[2] = swap ? wa[0] : wb[0];
+  w[3] = swap ? wa[1] : wb[1];
+  *reinterpret_cast<intx4_t*>(dst) = w;
+}
+
 } // namespace pgemm

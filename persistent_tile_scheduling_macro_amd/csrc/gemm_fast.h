@@ -58,7 +58,7 @@
 //   A, fp8:    BM rows (m) x 128 B; chunk c of row r at c ^ sa8(r),
 //              sa8(r) = ((r >> 1) & 1) | (r & 4).
 //   B, 16-bit: 64 rows (k) x 2*BN B; chunk c of row r at
-//              c ^ (2*(r & 3) + 8*((r >> 3) & 1)).
+//              c ^ ((r & 1) + 4*((r >> 1) & 1) + 8*((r >> 3) & 1)).
 //   B, fp8:    128 rows (k) x BN B; chunk c of row r at
 //              c ^ ((r & 7) + 8*((r >> 5) & 1))          (BN = 256)
 //              c ^ (((r >> 1) & 3) + 4*((r >> 5) & 1))   (BN = 128).
@@ -68,7 +68,15 @@
 // consecutive k values.
 //
 // The MFMA is issued with B as its first operand, so each lane's four
-// outputs are four consecutive columns of one row of C (8-byte stores).
+// outputs of a block are four columns of one row of C. For the 16-bit types
+// the columns behind each MFMA block are permuted (n-position 4q + r of
+// block nb is wave column 32*(nb/2) + 8q + 4*((nb + q) & 1) + r) so that a
+// lane's outputs of blocks 2P and 2P+1 are eight consecutive columns: one
+// 16-byte store each, and two store instructions cover 64 bytes of each of
+// 16 rows. The transpose reads still fetch four consecutive columns per
+// source lane; the B swizzle above keeps them conflict-free with this
+// order. fp8 keeps the plain order (its transpose read hands out eight
+// consecutive columns per source lane) and stores 8 bytes per block.
 #pragma once
 
 #include "device_common.h"
@@ -94,7 +102,7 @@ struct Tile<kTile128> {
 // Swizzle of B's LDS rows: row k's chunk c is stored at chunk c ^ b_swz(k).
 template <int ES, int B_ROW>
 __host__ __device__ constexpr int b_swz(int k) {
-  return ES == 2 ? 2 * (k & 3) + 8 * ((k >> 3) & 1)
+  return ES == 2 ? (k & 1) + 4 * ((k >> 1) & 1) + 8 * ((k >> 3) & 1)
                  : (B_ROW == 256 ? (k & 7) + 8 * ((k >> 5) & 1) : ((k >> 1) & 3) + 4 * ((k >> 5) & 1));
 }
 
@@ -240,9 +248,12 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, 2) gemm_fast_kernel(Par
     // the swizzle is the same for every row this lane reads from here
     // (+4 and +32 rows for 16-bit, +8/+16/+24 for fp8)
     if constexpr (ES == 2) {
+      // source lane q = s16 & 3 of a row reads the four columns at wave
+      // column 32*(nb/2) + 8q + 4*((nb + q) & 1) (permuted order)
       const int k = 8 * g + (s16 >> 2);
-      const int Lc = wn * 8 + 2 * nb + ((s16 & 3) >> 1);
-      b_off[nb] = k * B_ROW + 16 * (Lc ^ b_swz<ES, B_ROW>(k)) + 8 * (s16 & 1);
+      const int q = s16 & 3;
+      const int Lc = wn * 8 + 4 * (nb >> 1) + q;
+      b_off[nb] = k * B_ROW + 16 * (Lc ^ b_swz<ES, B_ROW>(k)) + 8 * ((nb + q) & 1);
     } else {
       const int k = 32 * g + (s16 >> 1);
       const int Lc = wn * 4 + nb;
@@ -372,22 +383,52 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, 2) gemm_fast_kernel(Par
     int pm, pn;
     tile_coords(tile, p, &pm, &pn);
     const int mrow = pm * BM + wm * WTM + s16;
-    const int ncol = pn * BN + wn * 64 + 4 * g;
     out_t* C = reinterpret_cast<out_t*>(p.C);
+    if constexpr (ES == 2) {
+      // permuted order: blocks 2P and 2P+1 give this lane columns
+      // 32P + 8g .. +7 (block 2P + (g & 1) the first four). N is a multiple
+      // of 8, so each 16-byte store is wholly inside or outside C. Interior
+      // tiles (the uniform common case) store without masks; the schedule
+      // barriers keep each row block's accumulator reads next to its stores.
+      const int ncol8 = pn * BN + wn * 64 + 8 * g;
+      const bool odd = (g & 1) != 0;
+      out_t* crow = C + (int64_t)mrow * ldc + ncol8;
+      if ((pm * BM + BM <= M) & (pn * BN + BN <= N)) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int m = mrow + mb * 16;
-      if (m < M) {
+        for (int mb = 0; mb < MB; ++mb) {
+          out_t* dst = crow + (int64_t)(16 * mb) * ldc;
+          store8(dst, acc[mb][0], acc[mb][1], odd);
+          store8(dst + 32, acc[mb][2], acc[mb][3], odd);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const int n = ncol + nb * 16;
-          out_t* dst = C + (int64_t)m * ldc + n;
-          if (n + 3 < N) {
-            store4(dst, acc[mb][nb]);
-          } else {
+        for (int mb = 0; mb < MB; ++mb) {
+          if (mrow + mb * 16 < M) {
+            out_t* dst = crow + (int64_t)(16 * mb) * ldc;
+            if (ncol8 < N) store8(dst, acc[mb][0], acc[mb][1], odd);
+            if (ncol8 + 32 < N) store8(dst + 32, acc[mb][2], acc[mb][3], odd);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    } else {
+      const int ncol = pn * BN + wn * 64 + 4 * g;
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (n + e < N) dst[e] = to_out(acc[mb][nb][e], (out_t*)nullptr);
+      for (int mb = 0; mb < MB; ++mb) {
+        const int m = mrow + mb * 16;
+        if (m < M) {
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) {
+            const int n = ncol + nb * 16;
+            out_t* dst = C + (int64_t)m * ldc + n;
+            if (n + 3 < N) {
+              store4(dst, acc[mb][nb]);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (n + e < N) dst[e] = to_out(acc[mb][nb][e], (out_t*)nullptr);
+            }
           }
         }
       }

@@ -88,7 +88,7 @@ bool sizes_fast(int dtype, int64_t N, int64_t K) {
 }
 
 bool ptrs_fast(const void* A, const void* B, const void* C) {
-  return ((uintptr_t)A % 16) == 0 && ((uintptr_t)B % 16) == 0 && ((uintptr_t)C % 8) == 0;
+  return ((uintptr_t)A % 16) == 0 && ((uintptr_t)B % 16) == 0 && ((uintptr_t)C % 16) == 0;
 }
 
 struct Plan {
