@@ -284,42 +284,66 @@ def main():
 
 
 def cpu_baseline(dtype, kind, wid, probs, seconds):
-    """Time the CPU oracle (as it stands) on a bounded row sample of the same workload."""
+    """Time the CPU oracle (as it stands) on a bounded sample of the same workload:
+    whole problems of the sweep, largest K first, until about `seconds` have
+    been spent (row-sampled when even the first problem would take far longer)."""
     import numpy as np
 
     import oracle
     import seeded_inputs as si
 
     cores = oracle.default_threads()
-    # one mode's worth of distinct (M, N, K) problems, largest K first
-    seen = []
+    shapes = {}
     for (m, n, K, _, _) in probs:
-        if (m, n, K) not in seen:
-            seen.append((m, n, K))
-    m, n, K = max(seen, key=lambda x: x[2])
-    A, B = si.operands(m, n, K, dtype, kind, workload=wid)
-    Ab, Bb = si.bits(A), si.bits(B)
-    # Each call decodes all of B once before the row loop, so time two row
-    # counts and size the sample from the per-row slope to take about `seconds`.
-    def timed(r):
+        shapes.setdefault((m, n), set()).add(K)
+    todo = sorted({(m, n, K) for (m, n), ks in shapes.items() for K in ks}, key=lambda x: -x[2])
+    drawn = {}
+
+    def bits_of(m, n, K):
+        kmax = max(shapes[(m, n)])
+        if (m, n) not in drawn:
+            drawn.clear()
+            drawn[(m, n)] = si.operands(m, n, kmax, dtype, kind, workload=wid)
+        A, B = drawn[(m, n)]
+        return si.bits(A[:, :K].contiguous()), si.bits(B[:K, :].contiguous())
+
+    # cost of the first (largest) problem from two row counts (each call also decodes all of B)
+    m, n, K = todo[0]
+    Ab, Bb = bits_of(m, n, K)
+
+    def timed_rows(r):
         t0 = time.perf_counter()
         oracle.gemm(Ab, Bb, dtype, rows=np.arange(r) * (m // r), nthreads=cores)
         return time.perf_counter() - t0
 
     r1, r2 = 16, 64
-    t1, t2 = timed(r1), timed(r2)
+    t1, t2 = timed_rows(r1), timed_rows(r2)
     per_row = max((t2 - t1) / (r2 - r1), t2 / r2 / 4, 1e-9)
     fixed = max(t1 - r1 * per_row, 0.0)
-    nrows = int(min(m, max(r2, (seconds - fixed) / per_row)))
-    rng = np.random.default_rng(0)
-    sample = np.sort(rng.choice(m, size=nrows, replace=False))
-    t0 = time.perf_counter()
-    oracle.gemm(Ab, Bb, dtype, rows=sample, nthreads=cores)
-    t = time.perf_counter() - t0
-    fl = 2.0 * nrows * n * K
-    return {"value": round(fl / t / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{nrows} of {m} rows of the {m}x{n}x{K} {dtype} problem, all {n} columns, "
-                      f"fp64 triple loop, {t:.1f} s"}
+    flops = 0.0
+    spent = 0.0
+    done = []
+    if fixed + m * per_row > 2 * seconds:  # one problem is too big: sample its rows
+        nrows = int(min(m, max(r2, (seconds - fixed) / per_row)))
+        rows = np.sort(np.random.default_rng(0).choice(m, size=nrows, replace=False))
+        t0 = time.perf_counter()
+        oracle.gemm(Ab, Bb, dtype, rows=rows, nthreads=cores)
+        spent = time.perf_counter() - t0
+        flops = 2.0 * nrows * n * K
+        sample = f"{nrows} of {m} rows of the {m}x{n}x{K} {dtype} problem, all {n} columns"
+    else:
+        for (m, n, K) in todo:
+            if spent >= seconds:
+                break
+            Ab, Bb = bits_of(m, n, K)
+            t0 = time.perf_counter()
+            oracle.gemm(Ab, Bb, dtype, nthreads=cores)
+            spent += time.perf_counter() - t0
+            flops += 2.0 * m * n * K
+            done.append(f"{m}x{n}x{K}")
+        sample = f"{len(done)} of the {len(todo)} problems of the workload in full ({', '.join(done)})"
+    return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{sample}, fp64 triple loop, {spent:.1f} s"}
 
 
 if __name__ == "__main__":

@@ -175,6 +175,18 @@ __device__ inline void mfma_acc(floatx4_t& c, const intx8_t& a, const intx8_t& b
 // of their results (the compiler cannot see the asm's latency).
 __device__ inline void acc_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 
+// Read an accumulator block out of its AGPRs at this point of the program.
+// (Left to itself the compiler copies the whole 128-register accumulator
+// tile into VGPRs ahead of the epilogue and spills around it.)
+__device__ inline floatx4_t acc_read(const floatx4_t& a) {
+  floatx4_t v;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v[0]) : "a"(a[0]));
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v[1]) : "a"(a[1]));
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v[2]) : "a"(a[2]));
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v[3]) : "a"(a[3]));
+  return v;
+}
+
 // --------------------------------------------------------- output rounding
 // fp32 -> fp16 / bf16, IEEE round to nearest even.
 __device__ inline _Float16 to_out(float x, _Float16*) { return (_Float16)x; }

@@ -397,8 +397,8 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, 2) gemm_fast_kernel(Par
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           out_t* dst = crow + (int64_t)(16 * mb) * ldc;
-          store8(dst, acc[mb][0], acc[mb][1], odd);
-          store8(dst + 32, acc[mb][2], acc[mb][3], odd);
+          store8(dst, acc_read(acc[mb][0]), acc_read(acc[mb][1]), odd);
+          store8(dst + 32, acc_read(acc[mb][2]), acc_read(acc[mb][3]), odd);
           __builtin_amdgcn_sched_barrier(0);
         }
       } else {
@@ -406,8 +406,8 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, 2) gemm_fast_kernel(Par
         for (int mb = 0; mb < MB; ++mb) {
           if (mrow + mb * 16 < M) {
             out_t* dst = crow + (int64_t)(16 * mb) * ldc;
-            if (ncol8 < N) store8(dst, acc[mb][0], acc[mb][1], odd);
-            if (ncol8 + 32 < N) store8(dst + 32, acc[mb][2], acc[mb][3], odd);
+            if (ncol8 < N) store8(dst, acc_read(acc[mb][0]), acc_read(acc[mb][1]), odd);
+            if (ncol8 + 32 < N) store8(dst + 32, acc_read(acc[mb][2]), acc_read(acc[mb][3]), odd);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -423,7 +423,7 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, 2) gemm_fast_kernel(Par
             const int n = ncol + nb * 16;
             out_t* dst = C + (int64_t)m * ldc + n;
             if (n + 3 < N) {
-              store4(dst, acc[mb][nb]);
+              store4(dst, acc_read(acc[mb][nb]));
             } else {
 #pragma unroll
               for (int e = 0; e < 4; ++e)
