@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "e4m3fn": 5033.2}  # dense MFMA, 256 CU x 2.4 GHz
 HBM_GBS = 8000.0
 ESIZE = {"f16": 2, "bf16": 2, "e4m3fn": 1}
-MODE_NAMES = {0: "nonpersistent", 1: "static", 2: "dynamic"}
+MODE_NAMES = {0: "nonpersistent", 1: "static", 2: "dynamic", 3: "cancel"}
 
 WORKLOADS = {
     # name: (description, dtype, M, N, K list, modes, grid multiples, input kind, workload id)
@@ -44,6 +44,9 @@ WORKLOADS = {
              "bf16", None, None, [4000, 6144, 8200], [0, 1, 2], [0], "normal", 5),
     "square8k": ("fp16 GEMM M=N=K=8192, uniform[-1,1], fp16 C; all modes", "f16", 8192, 8192, [8192],
                  [0, 1, 2], [0], "uniform", 3),
+    "uneven": ("fp16 GEMM M=N=K=8192, uniform[-1,1], fp16 C; all four scheduling modes, alone and while "
+               "--hold-cus CUs are held by a co-running kernel", "f16", 8192, 8192, [8192],
+               [0, 1, 2, 3], [0], "uniform", 3),
 }
 
 
@@ -57,6 +60,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample duration")
     ap.add_argument("--modes", default=None, help="comma-separated subset of scheduling modes (0,1,2)")
+    ap.add_argument("--hold-cus", type=int, default=64, help="uneven workload: CUs held by the co-running kernel")
+    ap.add_argument("--hold-us", type=int, default=6000, help="uneven workload: how long they are held")
     ap.add_argument("--tile", default="auto", choices=["auto", "256", "128"],
                     help="macro tile of the fast kernel (auto: the library's default choice)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -146,6 +151,8 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.workload == "uneven":
+        return run_uneven(args, pg, si, torch, np)
     desc, dtype, kind, wid, probs = problems(args.workload)
     if args.modes:
         keep = {int(x) for x in args.modes.split(",")}
@@ -236,7 +243,7 @@ def main():
     dom = max(tot, key=lambda k: tot[k][0])
     dom_time, dom_flops, dom_n = tot[dom]
     achieved = dom_flops / dom_time / 1e12
-    sched_names = {0: "kNonPersistent", 1: "kStatic", 2: "kDynamic"}
+    sched_names = {0: "kNonPersistent", 1: "kStatic", 2: "kDynamic", 3: "kCancel"}
     dt_name = {"f16": "kF16", "bf16": "kBF16", "e4m3fn": "kF8E4M3"}[dtype]
     if dom[1]:
         kname = f"gemm_fast_kernel<{dt_name}, {sched_names[dom[0]]}, kTile{dom[1]}>"
@@ -276,6 +283,76 @@ def main():
                  for k, v in sorted(best.items())[-3:]},
         "roofline": roofline,
         "cpu_baseline": cpu,
+    }
+    if args.table:
+        with open(args.table, "w") as f:
+            json.dump({"result": result, "table": table}, f, indent=1)
+    print(json.dumps(result), flush=True)
+
+
+def run_uneven(args, pg, si, torch, np):
+    """The schedulers when part of the GPU is busy (KernelWiki "Persistent Kernels
+    with Cluster Launch Control", "Choosing between static and CLC scheduling": a
+    static mapping assumes every CU is available). Each timed GEMM is launched while
+    a kernel on a second stream holds `--hold-cus` CUs for `--hold-us`; the same
+    GEMMs are also timed alone. Timing is per launch with HIP events on the GEMM's
+    stream, which include any wait for CUs."""
+    desc, dtype, kind, wid, probs = problems("uneven")
+    M = N = K = 8192
+    dev = torch.device("cuda:0")
+    A, B = si.operands(M, N, K, dtype, kind, workload=wid)
+    A, B = A.to(dev), B.to(dev)
+    C = torch.empty((M, N), dtype=torch.float16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    side = torch.cuda.Stream(device=dev)  # default priority
+    h = pg.pgemm_create(0)
+    pg.pgemm_set_stream(h, stream)
+    modes = [0, 1, 2, 3]
+    if args.modes:
+        modes = [m for m in modes if m in {int(x) for x in args.modes.split(",")}]
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    held_set = [0, min(args.hold_cus, cus - 1)]
+    times = {(hc, m): [] for hc in held_set for m in modes}
+
+    def one(hc, m):
+        if hc:
+            pg.pgemm_hold_cus(side, 0, hc, args.hold_us)
+            time.sleep(0.0005)  # let the holding workgroups take their CUs first
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        pg.pgemm_run(h, A, B, C, M, N, K, pg.PGEMM_F16, m, 0)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3
+
+    for _ in range(args.warmup):
+        for hc in held_set:
+            for m in modes:
+                one(hc, m)
+    for _ in range(args.steps):
+        for hc in held_set:
+            for m in modes:
+                times[(hc, m)].append(one(hc, m))
+    flops = 2.0 * M * N * K
+    table = []
+    for (hc, m), ts in times.items():
+        t = float(np.median(ts))
+        info = pg.pgemm_query_launch(h, M, N, K, pg.PGEMM_F16, m, 0)
+        table.append({"held_cus": hc, "mode": MODE_NAMES[m], "us": round(t * 1e6, 1),
+                      "tflops": round(flops / t / 1e12, 1), "tiles": info["tiles"], "grid": info["grid"]})
+    pg.pgemm_destroy(h)
+    tot_t = sum(sum(ts) for ts in times.values())
+    n_runs = sum(len(ts) for ts in times.values())
+    value = flops * n_runs / tot_t / 1e12
+    result = {
+        "metric": "GEMM TFLOPS and % of dense MFMA peak vs K; persistent vs non-persistent",
+        "value": round(value, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(tot_t / args.steps * 1e3, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": dtype, "data": "synthetic",
+        "config": {"workload": desc, "name": "uneven", "hold_cus": held_set[1], "hold_us": args.hold_us,
+                   "cus": cus},
+        "by_mode": {f"{r['mode']}@held{r['held_cus']}": r["tflops"] for r in table},
+        "roofline": None, "cpu_baseline": None,
     }
     if args.table:
         with open(args.table, "w") as f:

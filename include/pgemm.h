@@ -21,7 +21,7 @@
  * errors of the launch itself are returned as PGEMM_ERR_HIP, with detail
  * in pgemm_last_error(). A handle is not thread-safe: use one handle per
  * stream used concurrently (the dynamic scheduler's work counter is per
- * handle).
+ * handle; DYNAMIC and CANCEL share it).
  */
 #ifndef PGEMM_H
 #define PGEMM_H
@@ -64,11 +64,20 @@ typedef enum {
  *   w, then claims further tile ids from a device-wide atomic work counter
  *   until a claim fails, after which it never claims again -- the AMD
  *   analogue of cluster launch control's cancel-and-reuse (KernelWiki,
- *   intro), not a port of it. */
+ *   intro), not a port of it.
+ * CANCEL: the grid is one workgroup per tile (T), as in NONPERSISTENT, but
+ *   every workgroup claims its tiles -- the first one too -- from the work
+ *   counter and keeps claiming until a claim fails. Workgroups that run
+ *   early take over the tiles of workgroups that have not started; those
+ *   find no tile left when they start and exit at once. This is the closer
+ *   analogue of cancel-and-reuse (a grid whose not-yet-launched members'
+ *   ids are taken over, same page, intro) and needs no co-residency
+ *   assumption; grid_multiple is ignored. */
 typedef enum {
   PGEMM_SCHED_NONPERSISTENT = 0,
   PGEMM_SCHED_STATIC = 1,
-  PGEMM_SCHED_DYNAMIC = 2
+  PGEMM_SCHED_DYNAMIC = 2,
+  PGEMM_SCHED_CANCEL = 3
 } pgemm_sched_t;
 
 /* Macro-tile configurations of the fast kernel (the Triton persistent-
@@ -88,8 +97,8 @@ typedef enum {
 } pgemm_tile_t;
 
 /* Create a handle on HIP device `device` (which becomes current). Allocates
- * the dynamic scheduler's device work counter (zeroed) and caches the CU
- * count. The handle starts on the null stream. *out is NULL on failure. */
+ * the claiming modes' device work counter (zeroed) and caches the CU count.
+ * The handle starts on the null stream. *out is NULL on failure. */
 int pgemm_create(pgemm_handle_t* out, int device);
 
 /* Bind a hipStream_t (passed as void*; NULL = null stream). Later runs
@@ -104,7 +113,8 @@ int pgemm_set_stream(pgemm_handle_t h, void* hip_stream);
  *     K == 0: C is filled with zeros (an empty sum).
  *   dtype: pgemm_dtype_t.
  *   sched_mode: pgemm_sched_t.
- *   grid_multiple: persistent modes only (ignored for NONPERSISTENT).
+ *   grid_multiple: persistent modes only (ignored for NONPERSISTENT and
+ *     CANCEL).
  *     <= 0: G = occupancy x CU count (all workgroups co-resident, the
  *     sizing of the forum thread's first answer); > 0: G = grid_multiple x
  *     CU count (the NUM_SMS multiple of the Triton issue's follow-up
@@ -171,9 +181,23 @@ int pgemm_set_tile_config(pgemm_handle_t h, int tile);
 int pgemm_tile_coords(int64_t t, int64_t n_m, int64_t n_n, int group_m, int cu_chunk, int* pid_m,
                       int* pid_n);
 
-/* Read the device work counter (synchronizes the handle's stream). It
- * reads 0 between launches; any other value means a launch was cut short. */
+/* Read the device work counter of the claiming modes (synchronizes the
+ * handle's stream). It reads 0 between launches -- each launch's last claim
+ * resets it -- so any other value means a launch was cut short. */
 int pgemm_read_work_counter(pgemm_handle_t h, int32_t* value);
+
+/* Benchmark aid, not part of the GEMM: make about `n_cus` CUs of device
+ * `device` unavailable for about `microseconds`, asynchronously on the HIP
+ * stream `hip_stream` (NULL = null stream). It launches n_cus workgroups
+ * that each hold a whole CU's LDS (so no GEMM workgroup can share that CU)
+ * and idle until the device's constant-rate clock has advanced by the
+ * given time; the wait is also capped by a pass count, so the kernel ends
+ * even if that clock stalled. Used to measure the schedulers when only part
+ * of the GPU is available (KernelWiki "Persistent Kernels with Cluster
+ * Launch Control", "Choosing between static and CLC scheduling"). n_cus in
+ * [0, 65536], microseconds in [0, 10^6], else PGEMM_ERR_INVALID_ARG; 0 for
+ * either launches nothing. */
+int pgemm_hold_cus(void* hip_stream, int device, int n_cus, int microseconds);
 
 #ifdef __cplusplus
 }

@@ -27,6 +27,7 @@ PGEMM_F8E4M3_BF16 = 2
 PGEMM_SCHED_NONPERSISTENT = 0
 PGEMM_SCHED_STATIC = 1
 PGEMM_SCHED_DYNAMIC = 2
+PGEMM_SCHED_CANCEL = 3
 
 PGEMM_TILE_AUTO = 0
 PGEMM_TILE_256 = 1
@@ -34,7 +35,7 @@ PGEMM_TILE_128 = 2
 
 DTYPE_NAMES = {"f16": PGEMM_F16, "bf16": PGEMM_BF16, "e4m3fn": PGEMM_F8E4M3_BF16}
 SCHED_NAMES = {"nonpersistent": PGEMM_SCHED_NONPERSISTENT, "static": PGEMM_SCHED_STATIC,
-               "dynamic": PGEMM_SCHED_DYNAMIC}
+               "dynamic": PGEMM_SCHED_DYNAMIC, "cancel": PGEMM_SCHED_CANCEL}
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with "
@@ -66,6 +67,7 @@ _set_tile_order = _sig("pgemm_set_tile_order", _int, _vp, _int, _int)
 _set_tile_config = _sig("pgemm_set_tile_config", _int, _vp, _int)
 _tile_coords = _sig("pgemm_tile_coords", _int, _i64, _i64, _i64, _int, _int, _ip, _ip)
 _read_work_counter = _sig("pgemm_read_work_counter", _int, _vp, ctypes.POINTER(_i32))
+_hold_cus = _sig("pgemm_hold_cus", _int, _vp, _int, _int, _int)
 
 
 class PgemmError(RuntimeError):
@@ -104,11 +106,16 @@ def pgemm_create(device: int = 0):
     return h
 
 
-def pgemm_set_stream(h, stream) -> None:
-    """Bind a stream: a torch.cuda.Stream, a raw hipStream_t int, or None (null stream)."""
+def _stream_ptr(stream):
+    """hipStream_t of a torch.cuda.Stream, a raw int handle, or None (null stream)."""
     if stream is not None and not isinstance(stream, int):
         stream = int(stream.cuda_stream)
-    _check(_set_stream(h, stream or None), h)
+    return stream or None
+
+
+def pgemm_set_stream(h, stream) -> None:
+    """Bind a stream: a torch.cuda.Stream, a raw hipStream_t int, or None (null stream)."""
+    _check(_set_stream(h, _stream_ptr(stream)), h)
 
 
 def pgemm_run(h, A, B, C, M: int, N: int, K: int, dtype: int, sched_mode: int, grid_multiple: int = 0) -> None:
@@ -161,6 +168,11 @@ def pgemm_read_work_counter(h) -> int:
     v = ctypes.c_int32()
     _check(_read_work_counter(h, ctypes.byref(v)), h)
     return v.value
+
+
+def pgemm_hold_cus(stream, device: int, n_cus: int, microseconds: int) -> None:
+    """Benchmark aid: hold about n_cus CUs for about `microseconds` on `stream`."""
+    _check(_hold_cus(_stream_ptr(stream), int(device), int(n_cus), int(microseconds)))
 
 
 def matmul(A, B, C=None, *, sched: str | int = "static", grid_multiple: int = 0, handle=None):

@@ -29,7 +29,7 @@ typedef __fp16 fp16x4_raw_t __attribute__((__vector_size__(8)));
 #define PGEMM_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
 enum DType : int { kF16 = 0, kBF16 = 1, kF8E4M3 = 2 };
-enum Sched : int { kNonPersistent = 0, kStatic = 1, kDynamic = 2 };
+enum Sched : int { kNonPersistent = 0, kStatic = 1, kDynamic = 2, kCancel = 3 };
 
 // Per-dtype facts used by the kernels. A "k-group" is the reduction depth
 // of one MFMA: 32 for the 16-bit types (v_mfma_f32_16x16x32_{f16,bf16}),
@@ -104,24 +104,40 @@ __host__ __device__ inline void tile_coords(int t, const Params& p, int* pm, int
 }
 
 // ---------------------------------------------------- dynamic work counter
-// Claim protocol of the dynamic persistent mode. It is the AMD analogue of
-// cluster launch control (KernelWiki "Persistent Kernels with Cluster Launch
+// Claim protocol of the two claiming modes, the AMD analogue of cluster
+// launch control (KernelWiki "Persistent Kernels with Cluster Launch
 // Control", intro): the grid defines the candidate ids, a claim returns the
 // next unstarted id, and a failed claim means the worker never claims again.
-// Every workgroup starts on tile blockIdx.x without a claim; each further
-// claim returns counter+G. Each workgroup makes exactly one failing claim,
-// so one launch makes exactly T claims, returning the counter values
-// 0..T-1 once each; the claim that returns T-1 is the last one and resets
-// the counter to 0 for the next launch on the stream.
-// A counter value outside [0, T) cannot come from this protocol; it is
-// treated as a failed claim so a corrupted counter can never index a tile
-// outside the grid.
-// Host-callable too, so that a CPU test can race it from many threads.
-__host__ __device__ inline int claim_tile(int* counter, int T, int G) {
-  int c = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (c == T - 1) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return (c < 0 || c >= T) ? T : c + G;
+//
+// * dynamic persistent (grid G): every workgroup starts on tile blockIdx.x
+//   without a claim; claim value c names tile c + G.
+// * cancel-and-reuse (grid T): every workgroup claims even its first tile;
+//   claim value c names tile c. A workgroup that starts after every tile is
+//   taken fails its first claim and exits at once -- the stand-in for a
+//   cluster whose launch was cancelled and whose id was reused.
+//
+// Each workgroup makes exactly one failing claim, so a launch makes exactly
+// `total` claims (T for dynamic, T + G for cancel-and-reuse) and they return
+// the counter values 0..total-1 once each; the claim that returns total-1 is
+// the launch's last and resets the counter to 0 for the next launch on the
+// stream. A value outside [0, total) cannot come from this protocol and is
+// treated as a failed claim, so a corrupted counter never names a tile
+// outside the grid. (Claims are handed out in the order they arrive, which
+// at a launch's start is close to workgroup order, so the tiles a
+// workgroup gets are close to the ones the static mode would give it and
+// stay on the same XCD: workgroup w runs on XCD w % 8. Separate per-XCD
+// counters measured slower.) Host-callable too, so a CPU test can race it.
+__host__ __device__ inline int claim_tile(int* counter, int T, int offset, int total) {
+  const int c = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (c == total - 1) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return (c < 0 || c >= total || c + offset >= T) ? T : c + offset;
 }
+
+// Claim parameters of a scheduling mode: (offset, total) of claim_tile.
+template <int SCHED>
+__host__ __device__ inline int claim_offset(int G) { return SCHED == kCancel ? 0 : G; }
+template <int SCHED>
+__host__ __device__ inline int claim_total(int T, int G) { return SCHED == kCancel ? T + G : T; }
 
 // ------------------------------------------------ buffer loads into LDS
 // gfx9 buffer resource word 3 for raw (untyped) dword access.

@@ -263,28 +263,26 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, 2) gemm_fast_kernel(Par
 
   // ---- the tile sequence of this workgroup ---------------------------------
   // Sequence number q -> tile id. Static: blockIdx + q*G; non-persistent:
-  // blockIdx for q = 0 only; dynamic: blockIdx for q = 0, then each tile's
-  // successor is claimed when the producer starts copying that tile and is
-  // published in s_ring at the end of that step, before the next barrier.
-  int claim_val = 0;
-  bool claim_pending = false; // thread 0 only: a claim waiting to be published
-  int claim_seq = 0;          // sequence number the pending claim is for
+  // blockIdx for q = 0 only; dynamic: blockIdx for q = 0; cancel-and-reuse:
+  // claimed for q = 0 too. In the claiming modes thread 0 claims tile 1 (and
+  // tile 0) before the pipeline starts and then, in each tile's epilogue,
+  // the tile two ahead: the claim is issued before the C stores and its
+  // result written to s_ring after them, so the atomic's latency hides
+  // behind the stores, and the next barrier publishes it before the copy
+  // of that tile can begin. Keeping the claim code out of the k-loop keeps
+  // its registers out of the loop too.
+  constexpr bool CLAIMS = SCHED == kDynamic || SCHED == kCancel;
+  bool claim_live = false;    // thread 0 only: the last claim got a tile
   auto tile_of = [&](int q) __attribute__((always_inline)) -> int {
     if constexpr (SCHED == kNonPersistent) {
       return q == 0 ? (int)blockIdx.x : T;
     } else if constexpr (SCHED == kStatic) {
       const int64_t t = (int64_t)blockIdx.x + (int64_t)q * G;
       return t < T ? (int)t : T;
-    } else {
+    } else if constexpr (SCHED == kDynamic) {
       return q == 0 ? (int)blockIdx.x : __builtin_amdgcn_readfirstlane(s_ring[q & 7]);
-    }
-  };
-  auto publish_claim = [&]() __attribute__((always_inline)) {
-    if constexpr (SCHED == kDynamic) {
-      if (claim_pending) {
-        s_ring[claim_seq & 7] = claim_val;
-        claim_pending = false;
-      }
+    } else {
+      return __builtin_amdgcn_readfirstlane(s_ring[q & 7]);
     }
   };
 
@@ -307,13 +305,6 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, 2) gemm_fast_kernel(Par
       if (p_tile >= T) {
         p_done = true;
         return;
-      }
-      if constexpr (SCHED == kDynamic) {
-        if (tid == 0) { // claim the successor now; published after this step's MFMAs
-          claim_val = claim_tile(p.counter, T, G);
-          claim_seq = q + 1;
-          claim_pending = true;
-        }
       }
     }
     int pm, pn;
@@ -465,7 +456,6 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, 2) gemm_fast_kernel(Par
       if (mb == 3) copy_pair(ICN{}, std::integral_constant<int, 3>{});
       __builtin_amdgcn_sched_barrier(0);
     }
-    publish_claim();
     ++cs;
   };
   // mid-step variant (16-bit): the barrier sits between the two k-groups.
@@ -503,7 +493,6 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, 2) gemm_fast_kernel(Par
       read_a_frag(I0{}, sAn, 0, mb);
       __builtin_amdgcn_sched_barrier(0);
     }
-    publish_claim();
     ++cs;
   };
   auto step = [&](auto cst) __attribute__((always_inline)) {
@@ -518,21 +507,35 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, 2) gemm_fast_kernel(Par
     copy_pair(c, std::integral_constant<int, 2>{});
     copy_pair(c, std::integral_constant<int, 3>{});
   };
+  if constexpr (CLAIMS) {
+    if (tid == 0) {
+      int t0 = (int)blockIdx.x;
+      if constexpr (SCHED == kCancel) {
+        t0 = claim_tile(p.counter, T, claim_offset<SCHED>(G), claim_total<SCHED>(T, G));
+        s_ring[0] = t0;
+      }
+      const int t1 = t0 < T ? claim_tile(p.counter, T, claim_offset<SCHED>(G), claim_total<SCHED>(T, G)) : T;
+      s_ring[1] = t1;
+      claim_live = t1 < T;
+    }
+    __syncthreads();
+    if constexpr (SCHED == kCancel) {
+      // a workgroup that found no tile left exits here, all of it at once
+      if (tile_of(0) >= T) return;
+    }
+  }
   copy_whole(I0{}); // step 0 into stage 0
   if constexpr (KSUB == 2) {
     copy_whole(I1{}); // step 1 into stage 1 (nk >= 2: same tile)
-    publish_claim();
     wait_vmcnt<L>();  // step 0's copy landed; step 1's may still fly
     __syncthreads();
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) read_b_frag(I0{}, sB0, 0, nb);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) read_a_frag(I0{}, sA0, 0, mb);
-  } else {
-    publish_claim();
   }
   int c_q = 0; // consumer tile sequence number
-  int c_tile = blockIdx.x;
+  int c_tile = tile_of(0);
   for (;;) {
     zero_acc();
     for (int kt = 0; kt < nk; kt += 2) {
@@ -540,7 +543,18 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, 2) gemm_fast_kernel(Par
       step(I1{});
     }
     // tile finished: store it while the next tile's copies are in flight
+    // (claiming modes: and claim the tile two ahead meanwhile)
+    int claimed = T;
+    if constexpr (CLAIMS) {
+      if (tid == 0 && claim_live) {
+        claimed = claim_tile(p.counter, T, claim_offset<SCHED>(G), claim_total<SCHED>(T, G));
+        claim_live = claimed < T;
+      }
+    }
     epilogue(c_tile);
+    if constexpr (CLAIMS) {
+      if (tid == 0) s_ring[(c_q + 2) & 7] = claimed;
+    }
     if (!has_next) break;
     c_tile = tile_of(++c_q);
   }

@@ -8,7 +8,8 @@
 // the matrix), storing A as [m][k] and B transposed as [n][k] in LDS so
 // both fragments are contiguous reads. The tile schedulers are the same
 // three as the fast kernel's: one tile per workgroup, a static stride of G
-// over the tile order, or dynamic claims from the work counter.
+// over the tile order, or claims from the work counter (dynamic and
+// cancel-and-reuse).
 #pragma once
 
 #include "device_common.h"
@@ -39,6 +40,12 @@ __global__ void __launch_bounds__(THREADS) gemm_generic_kernel(Params p) {
   out_t* C = reinterpret_cast<out_t*>(p.C);
 
   int tile = blockIdx.x;
+  if constexpr (SCHED == kCancel) { // the first tile is claimed too
+    if (tid == 0) s_claim = claim_tile(p.counter, p.T, claim_offset<SCHED>(p.G), claim_total<SCHED>(p.T, p.G));
+    __syncthreads();
+    tile = __builtin_amdgcn_readfirstlane(s_claim);
+    __syncthreads();
+  }
   while (tile < p.T) {
     int pm, pn;
     tile_coords(tile, p, &pm, &pn);
@@ -105,7 +112,7 @@ __global__ void __launch_bounds__(THREADS) gemm_generic_kernel(Params p) {
     } else if constexpr (SCHED == kStatic) {
       tile += p.G;
     } else {
-      if (tid == 0) s_claim = claim_tile(p.counter, p.T, p.G);
+      if (tid == 0) s_claim = claim_tile(p.counter, p.T, claim_offset<SCHED>(p.G), claim_total<SCHED>(p.T, p.G));
       __syncthreads();
       tile = __builtin_amdgcn_readfirstlane(s_claim);
       __syncthreads();

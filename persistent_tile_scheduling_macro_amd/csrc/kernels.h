@@ -19,4 +19,8 @@ kernel_fn pick_kernel_f8(int sched, int body);
 // K == 0: C = 0 (an empty sum). n = M * N output elements.
 void launch_fill_zero(void* C, int64_t n, hipStream_t stream);
 
+// Benchmark aid (hold.hip): n workgroups that each hold a whole CU's LDS
+// until the constant-rate clock has advanced by `ticks`.
+void launch_hold(int n, uint64_t ticks, hipStream_t stream);
+
 } // namespace pgemm

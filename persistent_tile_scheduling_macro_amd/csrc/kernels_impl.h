@@ -22,7 +22,8 @@ kernel_fn pick_for_dtype(int sched, int body) {
   switch (sched) {
     case kNonPersistent: return pick_body<DT, kNonPersistent>(body);
     case kStatic: return pick_body<DT, kStatic>(body);
-    default: return pick_body<DT, kDynamic>(body);
+    case kDynamic: return pick_body<DT, kDynamic>(body);
+    default: return pick_body<DT, kCancel>(body);
   }
 }
 

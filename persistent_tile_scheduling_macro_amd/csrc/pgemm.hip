@@ -19,7 +19,7 @@ struct pgemm_ctx {
   int device = 0;
   hipStream_t stream = nullptr;
   int cus = 0;
-  int* counter = nullptr; // dynamic scheduler's work counter (device int32)
+  int* counter = nullptr; // work counter of the claiming modes (device int32)
   int32_t* visits = nullptr;
   int64_t n_visits = 0;
   int32_t* owner = nullptr;
@@ -127,8 +127,8 @@ int plan_launch(pgemm_ctx* h, int64_t M, int64_t N, int64_t K, int dtype, int sc
   if (e != hipSuccess) return fail(h, PGEMM_ERR_HIP, "occupancy query: %s", hipGetErrorString(e));
   if (occ < 1) occ = 1;
   pl->occupancy = occ;
-  if (sched == kNonPersistent) {
-    pl->G = pl->T;
+  if (sched == kNonPersistent || sched == kCancel) {
+    pl->G = pl->T; // one workgroup per tile (cancel-and-reuse: late ones find none left)
   } else {
     const int64_t mult = grid_multiple <= 0 ? occ : grid_multiple;
     pl->G = std::min<int64_t>(mult * h->cus, pl->T);
@@ -144,7 +144,7 @@ int check_common(pgemm_ctx* h, int64_t M, int64_t N, int64_t K, int dtype, int s
   if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX)
     return fail(h, PGEMM_ERR_UNSUPPORTED, "sizes must be below 2^31");
   if (dtype < PGEMM_F16 || dtype > PGEMM_F8E4M3_BF16) return fail(h, PGEMM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
-  if (sched < PGEMM_SCHED_NONPERSISTENT || sched > PGEMM_SCHED_DYNAMIC)
+  if (sched < PGEMM_SCHED_NONPERSISTENT || sched > PGEMM_SCHED_CANCEL)
     return fail(h, PGEMM_ERR_INVALID_ARG, "unknown sched_mode %d", sched);
   return PGEMM_OK;
 }
@@ -317,6 +317,16 @@ int pgemm_tile_coords(int64_t t, int64_t n_m, int64_t n_n, int group_m, int cu_c
   const int T = (int)(n_m * n_n);
   grouped_tile(xcd_remap((int)t, T, cu_chunk), (int)n_m, (int)n_n, group_m, pid_m, pid_n);
   return PGEMM_OK;
+}
+
+int pgemm_hold_cus(void* hip_stream, int device, int n_cus, int microseconds) {
+  if (n_cus < 0 || n_cus > 65536 || microseconds < 0 || microseconds > 1000000) return PGEMM_ERR_INVALID_ARG;
+  if (n_cus == 0 || microseconds == 0) return PGEMM_OK;
+  if (hipSetDevice(device) != hipSuccess) return PGEMM_ERR_INVALID_ARG;
+  int khz = 0; // rate of the s_memrealtime clock
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, device) != hipSuccess || khz <= 0) khz = 100000;
+  launch_hold(n_cus, (uint64_t)microseconds * (uint64_t)khz / 1000u, reinterpret_cast<hipStream_t>(hip_stream));
+  return hipGetLastError() == hipSuccess ? PGEMM_OK : PGEMM_ERR_HIP;
 }
 
 int pgemm_read_work_counter(pgemm_handle_t h, int32_t* value) {

@@ -1,16 +1,18 @@
-// Host race test of the dynamic tile scheduler's claim protocol.
+// Host race test of the claim protocol of the claiming tile schedulers.
 //
 // Compiled for the host only and linked with nothing from the library: it
 // includes the kernels' own header and calls the same claim_tile() the
-// dynamic persistent kernel calls, from G std::threads that stand in for the
-// G persistent workgroups. Each worker starts on tile w, then claims until a
-// claim fails (KernelWiki "Persistent Kernels with Cluster Launch Control",
-// intro: a failed request ends that worker's requests). Random sleeps vary
-// the interleavings.
+// claiming kernels call, from G std::threads that stand in for the G
+// workgroups. In the dynamic mode each worker starts on tile w, then claims;
+// in the cancel-and-reuse mode (G = T workers, started at staggered times)
+// each worker claims its first tile too and stops at once if none is left.
+// Either way a worker claims until a claim fails (KernelWiki "Persistent
+// Kernels with Cluster Launch Control", intro: a failed request ends that
+// worker's requests). Random sleeps vary the interleavings.
 //
-// usage: sched_sim <scenario> T G launches seed [arg]
+// usage: sched_sim <scenario> <dynamic|cancel> T G launches seed [arg]
 //   scenario "race":    plain launches back to back on one counter
-//   scenario "stall":   worker 0 sleeps `arg` ms before finishing its first tile
+//   scenario "stall":   worker 0 sleeps `arg` ms after starting its first tile
 //   scenario "corrupt": the counter is preset to `arg` before the first launch
 // Prints one line of key=value pairs; the pytest wrapper checks them.
 #include <atomic>
@@ -25,20 +27,24 @@
 #include "../persistent_tile_scheduling_macro_amd/csrc/device_common.h"
 
 int main(int argc, char** argv) {
-  if (argc < 6) {
-    std::fprintf(stderr, "usage: %s race|stall|corrupt T G launches seed [arg]\n", argv[0]);
+  using namespace pgemm;
+  if (argc < 7) {
+    std::fprintf(stderr, "usage: %s race|stall|corrupt dynamic|cancel T G launches seed [arg]\n", argv[0]);
     return 2;
   }
   const std::string scenario = argv[1];
-  const int T = std::atoi(argv[2]);
-  const int G = std::atoi(argv[3]);
-  const int launches = std::atoi(argv[4]);
-  const unsigned seed = (unsigned)std::strtoul(argv[5], nullptr, 10);
-  const long arg = argc > 6 ? std::atol(argv[6]) : 0;
+  const bool cancel = std::string(argv[2]) == "cancel";
+  const int T = std::atoi(argv[3]);
+  const int G = std::atoi(argv[4]);
+  const int launches = std::atoi(argv[5]);
+  const unsigned seed = (unsigned)std::strtoul(argv[6], nullptr, 10);
+  const long arg = argc > 7 ? std::atol(argv[7]) : 0;
   if (T < 1 || G < 1 || G > T || launches < 1) {
     std::fprintf(stderr, "need 1 <= G <= T and launches >= 1\n");
     return 2;
   }
+  const int offset = cancel ? claim_offset<kCancel>(G) : claim_offset<kDynamic>(G);
+  const int total = cancel ? claim_total<kCancel>(T, G) : claim_total<kDynamic>(T, G);
 
   alignas(64) int counter = scenario == "corrupt" ? (int)arg : 0;
   std::vector<std::atomic<int>> visits(T);
@@ -53,7 +59,18 @@ int main(int argc, char** argv) {
     for (int w = 0; w < G; ++w) {
       pool.emplace_back([&, w, l] {
         std::mt19937 rng(seed * 7919u + (unsigned)w * 104729u + (unsigned)l);
-        int t = w;  // first tile without a claim
+        auto claim = [&]() {
+          const int t = claim_tile(&counter, T, offset, total);
+          claims.fetch_add(1);
+          if (t >= T) failed.fetch_add(1);
+          return t;
+        };
+        int t = w;  // dynamic: first tile without a claim
+        if (cancel) {
+          // workgroups start at different times; the first tile is claimed
+          std::this_thread::sleep_for(std::chrono::microseconds(rng() % 2000));
+          t = claim();
+        }
         while (t < T) {
           visits[t].fetch_add(1);
           ++worker_tiles[w];
@@ -63,9 +80,7 @@ int main(int argc, char** argv) {
             std::this_thread::sleep_for(std::chrono::microseconds(rng() % 200));
           else
             std::this_thread::yield();
-          t = pgemm::claim_tile(&counter, T, G);
-          claims.fetch_add(1);
-          if (t >= T) failed.fetch_add(1);
+          t = claim();
         }
       });
     }
@@ -74,22 +89,21 @@ int main(int argc, char** argv) {
   }
 
   int vmin = 1 << 30, vmax = 0;
-  long vsum = 0, unvisited_first = 0;
+  long unvisited = 0;
   for (int t = 0; t < T; ++t) {
     const int v = visits[t].load();
     vmin = v < vmin ? v : vmin;
     vmax = v > vmax ? v : vmax;
-    vsum += v;
-    if (t >= G && v == 0) ++unvisited_first;
+    if (v == 0) ++unvisited;
   }
   int wmin = 1 << 30, wmax = 0;
   for (int w = 0; w < G; ++w) {
     wmin = worker_tiles[w] < wmin ? worker_tiles[w] : wmin;
     wmax = worker_tiles[w] > wmax ? worker_tiles[w] : wmax;
   }
-  std::printf("visits_min=%d visits_max=%d visits_sum=%ld claims=%ld failed=%ld worker0_tiles=%d "
-              "worker_tiles_min=%d worker_tiles_max=%d unvisited_beyond_G=%ld counter_after=",
-              vmin, vmax, vsum, claims.load(), failed.load(), worker_tiles[0], wmin, wmax, unvisited_first);
+  std::printf("visits_min=%d visits_max=%d unvisited=%ld claims=%ld failed=%ld worker0_tiles=%d "
+              "worker_tiles_min=%d worker_tiles_max=%d counter_after=",
+              vmin, vmax, unvisited, claims.load(), failed.load(), worker_tiles[0], wmin, wmax);
   for (int l = 0; l < launches; ++l) std::printf(l ? ",%d" : "%d", counter_after[l]);
   std::printf("\n");
   return 0;

@@ -86,3 +86,21 @@ def test_tile_coords_rejects_bad_arguments(pg):
         pg.pgemm_tile_coords(6, 2, 3, 1, 0)
     with pytest.raises(pg.PgemmError):
         pg.pgemm_tile_coords(0, 2, 3, 0, 0)
+
+
+def test_hold_cus_argument_checks(pg):
+    """The benchmark aid rejects out-of-range arguments before touching a
+    device, and launches nothing for zero CUs or zero time."""
+    for n, us in [(-1, 10), (70000, 10), (4, -1), (4, 2_000_000)]:
+        with pytest.raises(pg.PgemmError) as e:
+            pg.pgemm_hold_cus(None, 0, n, us)
+        assert e.value.status == pg.PGEMM_ERR_INVALID_ARG
+    pg.pgemm_hold_cus(None, 0, 0, 100)
+    pg.pgemm_hold_cus(None, 0, 8, 0)
+
+
+def test_cancel_mode_is_accepted_and_unknown_modes_are_not(pg):
+    assert pg.PGEMM_SCHED_CANCEL == 3
+    with pytest.raises(pg.PgemmError) as e:
+        pg.pgemm_run(None, 0, 0, 0, 1, 1, 1, 0, 3, 0)
+    assert e.value.status == pg.PGEMM_ERR_INVALID_ARG  # null handle, not an unknown mode

@@ -7,7 +7,7 @@ Checks, per case (see the oracle's header for what is computed):
   output type (every partial sum is an integer below 2^24, exact in fp32 in
   any order);
 * tile-visit counter: every output tile written exactly once;
-* C bitwise identical across the three modes (one tile body).
+* C bitwise identical across the four scheduling modes (one tile body).
 
 Every case runs with each macro-tile configuration of the fast kernel
 (256 x 256 and 128 x 128), selected explicitly through the C ABI.
@@ -24,7 +24,7 @@ pytestmark = pytest.mark.gpu
 DT = {"f16": 0, "bf16": 1, "e4m3fn": 2}
 OUT = {"f16": ("f16", torch.float16), "bf16": ("bf16", torch.bfloat16), "e4m3fn": ("bf16", torch.bfloat16)}
 TOL = {"f16": 2e-3, "bf16": 2e-3, "e4m3fn": 1e-2}
-MODES = [0, 1, 2]
+MODES = [0, 1, 2, 3]  # non-persistent, static, dynamic, cancel-and-reuse
 TILES = {"t256": 1, "t128": 2}  # PGEMM_TILE_256, PGEMM_TILE_128
 
 
@@ -139,8 +139,9 @@ def test_brute_force_tiny(pg, handle):
 
 
 def test_static_owner_map_and_dynamic_counter(pg, handle):
-    """Static: owner[t] = t mod G (deterministic mapping). Dynamic: every tile once,
-    the work counter back at 0 after each launch, also back to back."""
+    """Static: owner[t] = t mod G (deterministic mapping). Dynamic and
+    cancel-and-reuse: every tile once, the work counter back at 0 after each
+    launch, also back to back and interleaved with each other."""
     dev = torch.device("cuda:0")
     M, N, K = 8192, 4096, 64  # 512 tiles of 256 x 256 or 2048 of 128 x 128
     A, B = si.operands(M, N, K, "f16", "small_int", workload=3)
@@ -164,15 +165,30 @@ def test_static_owner_map_and_dynamic_counter(pg, handle):
     try:
         for rep in range(4):
             C = torch.empty((M, N), dtype=torch.float16, device=dev)
-            say(f"case dynamic back-to-back rep {rep}")
+            say(f"case dynamic / cancel back-to-back rep {rep}")
             pg.pgemm_run(handle, Ad, Bd, C, M, N, K, 0, 2, 1)
+            pg.pgemm_run(handle, Ad, Bd, C, M, N, K, 0, 3, 0)
             pg.pgemm_run(handle, Ad, Bd, C, M, N, K, 0, 2, 0)
             torch.cuda.synchronize()
             assert pg.pgemm_read_work_counter(handle) == 0
             assert np.array_equal(si.bits(C.cpu()), want)
-        assert np.array_equal(visits.cpu().numpy(), np.full(T, 8, np.int32))
+        assert np.array_equal(visits.cpu().numpy(), np.full(T, 12, np.int32))
     finally:
         pg.pgemm_set_tile_counter(handle, None)
+    # cancel-and-reuse: grid = T, every tile's owner is a workgroup of that grid
+    info = pg.pgemm_query_launch(handle, M, N, K, 0, 3, 0)
+    assert info["grid"] == info["tiles"] == T
+    owner = torch.full((T,), -1, dtype=torch.int32, device=dev)
+    pg.pgemm_set_owner_log(handle, owner)
+    try:
+        C = torch.empty((M, N), dtype=torch.float16, device=dev)
+        pg.pgemm_run(handle, Ad, Bd, C, M, N, K, 0, 3, 0)
+        torch.cuda.synchronize()
+    finally:
+        pg.pgemm_set_owner_log(handle, None)
+    o = owner.cpu().numpy()
+    assert o.min() >= 0 and o.max() < T
+    assert np.array_equal(si.bits(C.cpu()), want)
 
 
 def test_degenerate_sizes(pg, handle):
@@ -198,7 +214,7 @@ def test_invalid_arguments(pg, handle):
     with pytest.raises(pg.PgemmError):
         pg.pgemm_run(handle, A, A, A, 4, 8, 8, 7, 1, 0)
     with pytest.raises(pg.PgemmError):
-        pg.pgemm_run(handle, A, A, A, 4, 8, 8, 0, 5, 0)
+        pg.pgemm_run(handle, A, A, A, 4, 8, 8, 0, 4, 0)
     with pytest.raises(pg.PgemmError):
         pg.pgemm_run(handle, 0, A, A, 4, 8, 8, 0, 1, 0)
     small = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -209,3 +225,31 @@ def test_invalid_arguments(pg, handle):
             pg.pgemm_run(handle, big, big, big, 600, 600, 600, 0, 1, 0)  # 9 tiles > 1 counter
     finally:
         pg.pgemm_set_tile_counter(handle, None)
+
+
+def test_modes_while_cus_are_held(pg, handle):
+    """Every mode stays exact while another kernel holds half the CUs (its
+    workgroups then start late or wait for CUs): bit-exact small-integer C,
+    every tile written once, the work counter back at 0."""
+    dev = torch.device("cuda:0")
+    M, N, K = 2048, 2048, 512
+    A, B = si.operands(M, N, K, "f16", "small_int", workload=9)
+    want = oracle.round_to(oracle.gemm(si.bits(A), si.bits(B), "f16"), "f16")
+    Ad, Bd = A.to(dev), B.to(dev)
+    side = torch.cuda.Stream(device=dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    for mode in MODES:
+        T = pg.pgemm_query_launch(handle, M, N, K, 0, mode, 0)["tiles"]
+        visits = torch.zeros(T, dtype=torch.int32, device=dev)
+        C = torch.full((M, N), float("nan"), dtype=torch.float16, device=dev)
+        say(f"case held CUs mode {mode} T={T}")
+        pg.pgemm_set_tile_counter(handle, visits)
+        try:
+            pg.pgemm_hold_cus(side, 0, cus // 2, 2000)
+            pg.pgemm_run(handle, Ad, Bd, C, M, N, K, 0, mode, 0)
+            torch.cuda.synchronize()
+        finally:
+            pg.pgemm_set_tile_counter(handle, None)
+        assert bool(torch.all(visits == 1)), mode
+        assert np.array_equal(si.bits(C.cpu()), want), mode
+        assert pg.pgemm_read_work_counter(handle) == 0

@@ -1,23 +1,26 @@
-"""CPU race test of the dynamic scheduler's claim protocol (no GPU).
+"""CPU race test of the claim protocol of the claiming schedulers (no GPU).
 
-tests/sched_sim.cpp calls the kernels' own claim_tile() from G host threads
-standing in for the G persistent workgroups. What it must show, whatever
-the interleaving:
+tests/sched_sim.cpp calls the kernels' own claim_tile() from host threads
+standing in for the workgroups: G persistent workgroups that start on tile
+w (dynamic), or one per tile, started at staggered times, that claim their
+first tile too (cancel-and-reuse). What it must show, whatever the
+interleaving:
 
 * every tile is processed exactly once per launch;
-* a launch makes exactly T claims, of which exactly G fail (each worker's
-  last; KernelWiki "Persistent Kernels with Cluster Launch Control", intro:
-  a failed request means that worker never requests again);
-* the counter reads 0 after every launch, so launches on one stream need no
-  reset in between;
+* a launch makes exactly T (dynamic) or T + G (cancel-and-reuse) claims, of
+  which exactly G fail (each worker's last; KernelWiki "Persistent Kernels
+  with Cluster Launch Control", intro: a failed request means that worker
+  never requests again);
+* the counter reads 0 after every launch (the last claim resets it), so
+  launches on one stream need no reset in between;
 * a worker that stalls on its first tile does not hold back the rest: the
-  others take every remaining tile (the case where actual SM availability
-  differs from the static assumption, same page, "Choosing between static
-  and CLC scheduling");
+  others take every remaining tile (the case where the CUs actually
+  available differ from the static assumption, same page, "Choosing between
+  static and CLC scheduling");
 * a counter that does not read 0 at launch (a cut-short launch) is caught:
-  a value >= T makes every claim fail, which the tile-visit counter exposes
-  as unvisited tiles; a negative one only fails the first claims, and the
-  counter is then left non-zero after the launch.
+  a value >= the claim total makes every claim fail, which the tile-visit
+  counter exposes as unvisited tiles; a negative one only fails the first
+  claims, and the counter is then left non-zero after the launch.
 """
 import os
 import subprocess
@@ -41,8 +44,8 @@ def sim():
                                SRC, "-o", EXE + ".tmp"])
         os.replace(EXE + ".tmp", EXE)
 
-    def run(scenario, T, G, launches, seed, arg=None):
-        cmd = [EXE, scenario, str(T), str(G), str(launches), str(seed)] + ([str(arg)] if arg is not None else [])
+    def run(scenario, T, G, launches, seed, arg=None, mode="dynamic"):
+        cmd = [EXE, scenario, mode, str(T), str(G), str(launches), str(seed)] + ([str(arg)] if arg is not None else [])
         out = subprocess.run(cmd, capture_output=True, text=True, timeout=120, check=True).stdout
         kv = dict(item.split("=") for item in out.split())
         res = {k: int(v) for k, v in kv.items() if k != "counter_after"}
@@ -63,6 +66,30 @@ def test_exactly_once_and_counter_reset(sim, T, G, seed):
     assert r["counter_after"] == [0] * launches
 
 
+@pytest.mark.parametrize("T", [1, 5, 64, 300, 1089])
+@pytest.mark.parametrize("seed", [1, 2])
+def test_cancel_and_reuse_exactly_once(sim, T, seed):
+    """One worker per tile, claiming its first tile too: T successful claims, one
+    failing claim per worker, the counter back at 0 after every launch."""
+    launches = 2
+    r = sim("race", T, T, launches, seed, mode="cancel")
+    assert r["visits_min"] == launches and r["visits_max"] == launches
+    assert r["claims"] == 2 * T * launches
+    assert r["failed"] == T * launches
+    assert r["counter_after"] == [0] * launches
+
+
+def test_cancel_and_reuse_late_workers_take_nothing(sim):
+    """Worker 0 stalls on its first tile; the rest finish every other tile, and
+    workers that start late fail their first claim (they never get a tile)."""
+    T = 256
+    r = sim("stall", T, T, 1, 4, 300, mode="cancel")
+    assert r["visits_min"] == 1 and r["visits_max"] == 1
+    assert r["worker_tiles_min"] == 0  # some workers found no tile left at their start
+    assert r["worker0_tiles"] == 1
+    assert r["counter_after"] == [0]
+
+
 def test_stalled_worker_does_not_hold_back_the_rest(sim):
     T, G = 1024, 64
     r = sim("stall", T, G, 1, 5, 300)
@@ -77,7 +104,7 @@ def test_stale_counter_fails_every_claim(sim):
     r = sim("corrupt", T, G, 1, 3, 5000)
     # only the first tiles (no claim needed) are done; the visit counter shows the rest missing,
     # and the counter is left non-zero, which the host can read back
-    assert r["unvisited_beyond_G"] == T - G
+    assert r["unvisited"] == T - G
     assert r["failed"] == G and r["claims"] == G
     assert r["counter_after"] == [5000 + G]
 
