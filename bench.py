@@ -59,7 +59,9 @@ def parse():
     ap.add_argument("--table", default=None, help="write the per-(K, mode) table as JSON here")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample duration")
-    ap.add_argument("--modes", default=None, help="comma-separated subset of scheduling modes (0,1,2)")
+    ap.add_argument("--modes", default=None, help="comma-separated subset of scheduling modes (0,1,2,3)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured once as a HIP graph and replayed (launch overhead removed)")
     ap.add_argument("--hold-cus", type=int, default=64, help="uneven workload: CUs held by the co-running kernel")
     ap.add_argument("--hold-us", type=int, default=6000, help="uneven workload: how long they are held")
     ap.add_argument("--tile", default="auto", choices=["auto", "256", "128"],
@@ -206,6 +208,30 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    graph_info = None
+    if args.graph:
+        # One step captured as a graph: the launches are capture-safe (no memsets; the claiming
+        # modes' counter resets itself in the kernel). Replays timed with events on the stream.
+        gstream = torch.cuda.Stream(device=dev)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=gstream):
+            pg.pgemm_set_stream(h, gstream)
+            for p in probs:
+                launch(p)
+        pg.pgemm_set_stream(h, stream)
+        g.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(args.steps):
+            g.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        gt = g0.elapsed_time(g1) * 1e-3 / args.steps
+        graph_info = {"ms_per_step": round(gt * 1e3, 3),
+                      "value": round(sum(2.0 * p[0] * p[1] * p[2] for p in probs) / gt / 1e12, 1)}
+        del g
+
     flops = {p: 2.0 * p[0] * p[1] * p[2] for p in probs}
     per = {p: [] for p in probs}
     for s in range(args.steps):
@@ -284,6 +310,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if graph_info:
+        result["graph"] = graph_info
     if args.table:
         with open(args.table, "w") as f:
             json.dump({"result": result, "table": table}, f, indent=1)

@@ -253,3 +253,37 @@ def test_modes_while_cus_are_held(pg, handle):
         assert bool(torch.all(visits == 1)), mode
         assert np.array_equal(si.bits(C.cpu()), want), mode
         assert pg.pgemm_read_work_counter(handle) == 0
+
+
+def test_graph_capture_and_replay(pg):
+    """pgemm_run is capture-safe: no memsets, and the claiming modes' work
+    counter resets itself inside the kernel. A HIP graph holding one launch per
+    scheduling mode is replayed several times with eager work in between;
+    every replay's C is bit-exact and the counter reads 0 after each."""
+    dev = torch.device("cuda:0")
+    M, N, K = 1024, 768, 320
+    A, B = si.operands(M, N, K, "f16", "small_int", workload=13)
+    want = oracle.round_to(oracle.gemm(si.bits(A), si.bits(B), "f16"), "f16")
+    Ad, Bd = A.to(dev), B.to(dev)
+    Cs = [torch.empty((M, N), dtype=torch.float16, device=dev) for _ in MODES]
+    h = pg.pgemm_create(0)
+    try:
+        pg.pgemm_set_tile_config(h, pg.PGEMM_TILE_128)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            pg.pgemm_set_stream(h, torch.cuda.current_stream())
+            for C, mode in zip(Cs, MODES):
+                pg.pgemm_run(h, Ad, Bd, C, M, N, K, 0, mode, 0)
+        pg.pgemm_set_stream(h, torch.cuda.current_stream())
+        for rep in range(4):
+            for C in Cs:
+                C.fill_(float("nan"))  # eager work between replays
+            say(f"case graph replay {rep}")
+            g.replay()
+            torch.cuda.synchronize()
+            for C, mode in zip(Cs, MODES):
+                assert np.array_equal(si.bits(C.cpu()), want), (rep, mode)
+            assert pg.pgemm_read_work_counter(h) == 0
+    finally:
+        pg.pgemm_destroy(h)
