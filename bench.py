@@ -353,13 +353,19 @@ def run_uneven(args, pg, si, torch, np):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e-3
 
-    for _ in range(args.warmup):
+    # The clock sags over a burst of 8192^3 launches (power limit), so a fixed order
+    # would favour whichever mode runs first: the order rotates every step.
+    def order(s):
+        r = s % len(modes)
+        return modes[r:] + modes[:r]
+
+    for s in range(args.warmup):
         for hc in held_set:
-            for m in modes:
+            for m in order(s):
                 one(hc, m)
-    for _ in range(args.steps):
+    for s in range(args.steps):
         for hc in held_set:
-            for m in modes:
+            for m in order(s):
                 times[(hc, m)].append(one(hc, m))
     flops = 2.0 * M * N * K
     table = []
