@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "e4m3fn": 5033.2}  # dense MFMA, 256 CU x 2.4 GHz
 HBM_GBS = 8000.0
 ESIZE = {"f16": 2, "bf16": 2, "e4m3fn": 1}
-MODE_NAMES = {0: "nonpersistent", 1: "static", 2: "dynamic", 3: "cancel"}
+MODE_NAMES = {0: "nonpersistent", 1: "static", 2: "dynamic", 3: "cancel", 4: "streamk"}
 
 WORKLOADS = {
     # name: (description, dtype, M, N, K list, modes, grid multiples, input kind, workload id)
@@ -40,13 +40,16 @@ WORKLOADS = {
                 list(range(256, 8193, 256)), [0, 1, 2], [1, 2, 3], "uniform", 3),
     "fp8": ("fp8 e4m3 GEMM M=N=K=8192, uniform[-1,1] quantised with scale 1.0, bf16 C; static vs dynamic",
             "e4m3fn", 8192, 8192, [8192], [0, 1, 2], [0], "uniform", 4),
-    "tail": ("bf16 GEMM M=N=K in {4000, 6144, 8200}, normal(0,1), bf16 C; static vs dynamic (tail effect)",
-             "bf16", None, None, [4000, 6144, 8200], [0, 1, 2], [0], "normal", 5),
+    "tail": ("bf16 GEMM M=N=K in {4000, 6144, 8200}, normal(0,1), bf16 C; non-persistent, static, dynamic "
+             "and stream-K (tail effect)", "bf16", None, None, [4000, 6144, 8200], [0, 1, 2, 4], [0], "normal", 5),
+    "fewtiles": ("fp16 GEMM M=N=1024, K in {2048, 8192, 32768}, uniform[-1,1], fp16 C: fewer tiles than "
+                 "workgroups; non-persistent, static, dynamic and stream-K", "f16", 1024, 1024,
+                 [2048, 8192, 32768], [0, 1, 2, 4], [0], "uniform", 6),
     "square8k": ("fp16 GEMM M=N=K=8192, uniform[-1,1], fp16 C; all modes", "f16", 8192, 8192, [8192],
                  [0, 1, 2], [0], "uniform", 3),
-    "uneven": ("fp16 GEMM M=N=K=8192, uniform[-1,1], fp16 C; all four scheduling modes, alone and while "
+    "uneven": ("fp16 GEMM M=N=K=8192, uniform[-1,1], fp16 C; all five scheduling modes, alone and while "
                "--hold-cus CUs are held by a co-running kernel", "f16", 8192, 8192, [8192],
-               [0, 1, 2, 3], [0], "uniform", 3),
+               [0, 1, 2, 3, 4], [0], "uniform", 3),
 }
 
 
@@ -59,7 +62,7 @@ def parse():
     ap.add_argument("--table", default=None, help="write the per-(K, mode) table as JSON here")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample duration")
-    ap.add_argument("--modes", default=None, help="comma-separated subset of scheduling modes (0,1,2,3)")
+    ap.add_argument("--modes", default=None, help="comma-separated subset of scheduling modes (0..4)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured once as a HIP graph and replayed (launch overhead removed)")
     ap.add_argument("--hold-cus", type=int, default=64, help="uneven workload: CUs held by the co-running kernel")
@@ -269,7 +272,7 @@ def main():
     dom = max(tot, key=lambda k: tot[k][0])
     dom_time, dom_flops, dom_n = tot[dom]
     achieved = dom_flops / dom_time / 1e12
-    sched_names = {0: "kNonPersistent", 1: "kStatic", 2: "kDynamic", 3: "kCancel"}
+    sched_names = {0: "kNonPersistent", 1: "kStatic", 2: "kDynamic", 3: "kCancel", 4: "kStreamK"}
     dt_name = {"f16": "kF16", "bf16": "kBF16", "e4m3fn": "kF8E4M3"}[dtype]
     if dom[1]:
         kname = f"gemm_fast_kernel<{dt_name}, {sched_names[dom[0]]}, kTile{dom[1]}>"
@@ -279,6 +282,8 @@ def main():
                 "frac": round(achieved / peak, 4), "traffic": measured_traffic(kname, args.workload),
                 "kernel": kname, "launches": dom_n, "avg_us": round(dom_time / dom_n * 1e6, 2),
                 "flops_per_launch_avg": dom_flops / dom_n}
+    if dom[0] == 4:
+        roofline["note"] = "stream-K: each timed run is the GEMM kernel plus its fix-up launch"
 
     best = {}
     for row in table:
@@ -335,7 +340,7 @@ def run_uneven(args, pg, si, torch, np):
     side = torch.cuda.Stream(device=dev)  # default priority
     h = pg.pgemm_create(0)
     pg.pgemm_set_stream(h, stream)
-    modes = [0, 1, 2, 3]
+    modes = list(WORKLOADS["uneven"][5])
     if args.modes:
         modes = [m for m in modes if m in {int(x) for x in args.modes.split(",")}]
     cus = torch.cuda.get_device_properties(dev).multi_processor_count

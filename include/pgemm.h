@@ -11,10 +11,12 @@
  * (leading dimension N), C: M x N row-major (leading dimension N), all
  * contiguous, accumulated in fp32. The output is cut into macro tiles and
  * a tile scheduler hands tiles to workgroups (same question). Scheduling
- * never changes the value of C: every mode runs the same tile body, so C is
- * bitwise identical across modes and reruns (KernelWiki "Persistent
- * Kernels with Cluster Launch Control", "Choosing between static and CLC
- * scheduling": neither scheduler adds work).
+ * never changes the value of C: modes NONPERSISTENT..CANCEL run the same
+ * tile body, so C is bitwise identical across them and across reruns
+ * (KernelWiki "Persistent Kernels with Cluster Launch Control", "Choosing
+ * between static and CLC scheduling": neither scheduler adds work).
+ * STREAMK adds work (split tiles' partial sums), so its C may differ from
+ * theirs in the last bits; it is bitwise identical across its own reruns.
  *
  * Errors: every entry point returns a pgemm_status_t. No C++ exception
  * crosses this boundary. Launches are asynchronous on the handle's stream;
@@ -72,12 +74,30 @@ typedef enum {
  *   find no tile left when they start and exit at once. This is the closer
  *   analogue of cancel-and-reuse (a grid whose not-yet-launched members'
  *   ids are taken over, same page, intro) and needs no co-residency
- *   assumption; grid_multiple is ignored. */
+ *   assumption; grid_multiple is ignored.
+ * STREAMK: tail handling that creates work instead of idling CUs, for
+ *   tile counts T that the grid G does not divide (the case the KernelWiki
+ *   page's static-vs-CLC guidance leaves open: neither of its schedulers
+ *   creates work at the tail). With T = W*G + R, the first W*G tiles of the
+ *   tile order run whole, as in STATIC; the k-steps of the last R tiles are
+ *   split evenly over the G workgroups (over fewer when pieces would drop
+ *   below a minimum length), so every workgroup gets about W + R/G tiles
+ *   of work. A workgroup whose piece covers only part of a tile's k-range
+ *   writes an fp32 partial tile to a workspace the handle owns. A second
+ *   launch on the same stream then adds each split tile's partials in k
+ *   order, rounds the sum and stores the tile. G as in STATIC, without the
+ *   clamp to T: with T < G (W = 0) the split spreads even a few tiles over
+ *   the whole chip. The whole waves run as one STATIC launch over the first
+ *   W*G tiles, the tail as a second launch on its own grid, then the fix-up:
+ *   up to three launches per run, all on the handle's stream. R = 0 is
+ *   exactly STATIC (one launch). Operands that take the generic kernel
+ *   (below) run this mode as STATIC. */
 typedef enum {
   PGEMM_SCHED_NONPERSISTENT = 0,
   PGEMM_SCHED_STATIC = 1,
   PGEMM_SCHED_DYNAMIC = 2,
-  PGEMM_SCHED_CANCEL = 3
+  PGEMM_SCHED_CANCEL = 3,
+  PGEMM_SCHED_STREAMK = 4
 } pgemm_sched_t;
 
 /* Macro-tile configurations of the fast kernel (the Triton persistent-
@@ -119,16 +139,25 @@ int pgemm_set_stream(pgemm_handle_t h, void* hip_stream);
  *     sizing of the forum thread's first answer); > 0: G = grid_multiple x
  *     CU count (the NUM_SMS multiple of the Triton issue's follow-up
  *     comment), which may exceed co-residency -- no workgroup waits on
- *     another, so that stays correct. G is clamped to the tile count T.
+ *     another, so that stays correct. G is clamped to the tile count T
+ *     (except in STREAMK, see above).
  * Operands whose K and N are multiples of 16 bytes of elements (8 for
  * fp16/bf16, 16 for fp8) with 16-byte-aligned A, B and C
  * take the fast kernel (256 x 256 or 128 x 128 tiles, pgemm_tile_t);
  * others take a generic 64 x 64 tile kernel with the same schedulers
- * (correct, slower). */
+ * (correct, slower).
+ * STREAMK workspace: a run whose split needs more workspace than the handle
+ * holds (pgemm_query_streamk) first waits for the handle's stream, frees
+ * the old workspace and hipMallocs the new one (PGEMM_ERR_OOM if that
+ * fails); later runs of the same or smaller need allocate nothing. Under
+ * stream capture, make one such run before capturing. Two runs in flight
+ * on one handle share the workspace, which the one-stream-per-handle rule
+ * above already orders. */
 int pgemm_run(pgemm_handle_t h, const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
               int dtype, int sched_mode, int grid_multiple);
 
-/* Wait for the handle's stream, free the work counter and the handle.
+/* Wait for the handle's stream, free the work counter, the stream-K
+ * workspace and the handle.
  * NULL is accepted (no-op). */
 int pgemm_destroy(pgemm_handle_t h);
 
@@ -150,7 +179,12 @@ int pgemm_set_tile_counter(pgemm_handle_t h, int32_t* dev_visits, int64_t n_tile
 
 /* Attach a caller-owned device int32 array of n_tiles entries; each run
  * writes owner[t] = the id of the workgroup that computed tile t. NULL
- * detaches. Same size rule as the visit counter. */
+ * detaches. Same size rule as the visit counter. In STREAMK the W*G
+ * whole-wave tiles are logged by workgroup id of that launch (t mod G), a
+ * tail tile computed whole by the id of its workgroup in the tail launch,
+ * and a split tile, stored by the fix-up launch, as -1 - s (s = the tile's
+ * index among the R tail tiles); the visit counter counts that store, so
+ * every tile still reads 1. */
 int pgemm_set_owner_log(pgemm_handle_t h, int32_t* dev_owner, int64_t n_tiles);
 
 /* Report how pgemm_run would launch this problem, without launching:
@@ -161,6 +195,17 @@ int pgemm_set_owner_log(pgemm_handle_t h, int32_t* dev_owner, int64_t n_tiles);
 int pgemm_query_launch(pgemm_handle_t h, int64_t M, int64_t N, int64_t K, int dtype, int sched_mode,
                        int grid_multiple, int* tiles, int* grid, int* occupancy, int* bm, int* bn, int* bk,
                        int* fast_path);
+
+/* Report the STREAMK split pgemm_run would use for this problem, without
+ * launching: whole_tiles = W*G tiles run whole, split_tiles = R tail
+ * tiles whose k-steps are split, split_groups = workgroups sharing them,
+ * pieces_split = tail tiles actually cut into two or more pieces (0: no
+ * fix-up launch), workspace_bytes = the workspace the run needs (0 when
+ * nothing is cut). Output pointers may be NULL. Operands that take the
+ * generic kernel report split_tiles = 0. */
+int pgemm_query_streamk(pgemm_handle_t h, int64_t M, int64_t N, int64_t K, int dtype, int grid_multiple,
+                        int* whole_tiles, int* split_tiles, int* split_groups, int* pieces_split,
+                        int64_t* workspace_bytes);
 
 /* Tile-order knobs: GROUP_SIZE_M of the grouped order (default 4; the
  * Triton issue's setting is 8; 1 = row-major), and the XCD-aware remap

@@ -28,6 +28,7 @@ PGEMM_SCHED_NONPERSISTENT = 0
 PGEMM_SCHED_STATIC = 1
 PGEMM_SCHED_DYNAMIC = 2
 PGEMM_SCHED_CANCEL = 3
+PGEMM_SCHED_STREAMK = 4
 
 PGEMM_TILE_AUTO = 0
 PGEMM_TILE_256 = 1
@@ -35,7 +36,7 @@ PGEMM_TILE_128 = 2
 
 DTYPE_NAMES = {"f16": PGEMM_F16, "bf16": PGEMM_BF16, "e4m3fn": PGEMM_F8E4M3_BF16}
 SCHED_NAMES = {"nonpersistent": PGEMM_SCHED_NONPERSISTENT, "static": PGEMM_SCHED_STATIC,
-               "dynamic": PGEMM_SCHED_DYNAMIC, "cancel": PGEMM_SCHED_CANCEL}
+               "dynamic": PGEMM_SCHED_DYNAMIC, "cancel": PGEMM_SCHED_CANCEL, "streamk": PGEMM_SCHED_STREAMK}
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with "
@@ -63,6 +64,8 @@ _set_tile_counter = _sig("pgemm_set_tile_counter", _int, _vp, _vp, _i64)
 _set_owner_log = _sig("pgemm_set_owner_log", _int, _vp, _vp, _i64)
 _query_launch = _sig("pgemm_query_launch", _int, _vp, _i64, _i64, _i64, _int, _int, _int,
                      _ip, _ip, _ip, _ip, _ip, _ip, _ip)
+_query_streamk = _sig("pgemm_query_streamk", _int, _vp, _i64, _i64, _i64, _int, _int, _ip, _ip, _ip, _ip,
+                      ctypes.POINTER(_i64))
 _set_tile_order = _sig("pgemm_set_tile_order", _int, _vp, _int, _int)
 _set_tile_config = _sig("pgemm_set_tile_config", _int, _vp, _int)
 _tile_coords = _sig("pgemm_tile_coords", _int, _i64, _i64, _i64, _int, _int, _ip, _ip)
@@ -147,6 +150,17 @@ def pgemm_query_launch(h, M: int, N: int, K: int, dtype: int, sched_mode: int, g
                          *[ctypes.byref(o) for o in out]), h)
     keys = ["tiles", "grid", "occupancy", "bm", "bn", "bk", "fast_path"]
     return {k: o.value for k, o in zip(keys, out)}
+
+
+def pgemm_query_streamk(h, M: int, N: int, K: int, dtype: int, grid_multiple: int = 0) -> dict:
+    out = [ctypes.c_int() for _ in range(4)]
+    ws = _i64()
+    _check(_query_streamk(h, int(M), int(N), int(K), int(dtype), int(grid_multiple),
+                          *[ctypes.byref(o) for o in out], ctypes.byref(ws)), h)
+    keys = ["whole_tiles", "split_tiles", "split_groups", "pieces_split"]
+    d = {k: o.value for k, o in zip(keys, out)}
+    d["workspace_bytes"] = ws.value
+    return d
 
 
 def pgemm_set_tile_order(h, group_m: int = 8, xcd_remap: bool = True) -> None:

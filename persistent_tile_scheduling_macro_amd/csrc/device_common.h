@@ -1,6 +1,6 @@
 // Device-side building blocks shared by the GEMM kernels: element traits,
 // fragment types, buffer resources and zero-filling LDS loads, the tile
-// order, and the three tile schedulers.
+// order, the tile schedulers' claim protocol and the stream-K split.
 //
 // The operation is the GEMM of the persistent-kernel forum thread
 // (question): C = A*B cut into output tiles, each tile handed to one
@@ -29,7 +29,7 @@ typedef __fp16 fp16x4_raw_t __attribute__((__vector_size__(8)));
 #define PGEMM_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
 enum DType : int { kF16 = 0, kBF16 = 1, kF8E4M3 = 2 };
-enum Sched : int { kNonPersistent = 0, kStatic = 1, kDynamic = 2, kCancel = 3 };
+enum Sched : int { kNonPersistent = 0, kStatic = 1, kDynamic = 2, kCancel = 3, kStreamK = 4 };
 
 // Per-dtype facts used by the kernels. A "k-group" is the reduction depth
 // of one MFMA: 32 for the 16-bit types (v_mfma_f32_16x16x32_{f16,bf16}),
@@ -66,6 +66,12 @@ struct Params {
   int* counter;    // dynamic scheduler's work counter (reads 0 between launches)
   int* visits;     // optional int32[T] tile-visit counter
   int* owner;      // optional int32[T] owner log (workgroup id per tile)
+  // stream-K only (zero otherwise): the first T - sk_tiles tiles run whole,
+  // sk_waves per workgroup; the k-step pairs of the last sk_tiles tiles are
+  // split over workgroups 0 .. sk_groups-1; pieces that do not cover their
+  // whole tile leave fp32 partial tiles in `work` for the fix-up kernel.
+  int sk_waves, sk_tiles, sk_groups;
+  float* work;
 };
 
 // ------------------------------------------------------------ tile order
@@ -138,6 +144,105 @@ template <int SCHED>
 __host__ __device__ inline int claim_offset(int G) { return SCHED == kCancel ? 0 : G; }
 template <int SCHED>
 __host__ __device__ inline int claim_total(int T, int G) { return SCHED == kCancel ? T + G : T; }
+
+// ------------------------------------------------------ stream-K split
+// Tail handling that adds work units instead of idling CUs. With T = W*G + R
+// tiles on G workgroups the static mapping leaves the last wave R/G full;
+// the static and dynamic schedulers cannot fix that, because neither
+// creates more independent work than the tiles (KernelWiki "Persistent
+// Kernels with Cluster Launch Control", "Choosing between static and CLC
+// scheduling"). Here the first W*G tiles in tile order run whole (workgroup
+// w takes w, w+G, ..., as in the static mode) and the k-steps of the last R
+// tiles are laid end to end, in pairs (kp pairs per tile, so every piece
+// starts on stage 0 of the two-stage ring), and cut into sk_groups
+// contiguous ranges of equal length, one per workgroup:
+//   range of workgroup w: pair positions [w*S/Gs, (w+1)*S/Gs), S = R*kp.
+// A range crosses tile boundaries, so it is a sequence of pieces, each the
+// part of one tile's k-range that lies in it. A piece that is a whole tile
+// is stored to C as usual; any other piece stores its fp32 partial tile in
+// workspace slot w + s (s = tile - W*G): along the pair positions each new
+// piece starts at a workgroup boundary or a tile boundary, so w + s grows
+// by at least one from piece to piece and the slots of distinct pieces
+// differ. A fix-up launch then adds each split tile's partials in k order
+// (deterministic: the same bits on every run) and rounds them to C. The
+// split needs 1 <= Gs <= S, so that every range holds at least one pair
+// and the workgroups w0..w1 of a split tile all left a partial in it.
+
+// Workgroup whose range holds pair position x: the w with
+// floor(w*S/Gs) <= x < floor((w+1)*S/Gs), i.e. ceil((x+1)*Gs/S) - 1.
+__host__ __device__ inline int sk_owner(int64_t x, int64_t S, int Gs) {
+  return (int)(((x + 1) * Gs + S - 1) / S - 1);
+}
+__host__ __device__ inline int64_t sk_range_begin(int w, int64_t S, int Gs) { return (int64_t)w * S / Gs; }
+
+// Work unit q of workgroup w: sets tile, and the k-step range [kb, ke) of
+// it (even numbers; nk = 2*kp is a whole tile); returns false past the
+// workgroup's last unit. G = launch grid, W = whole-tile waves.
+__host__ __device__ inline bool sk_unit(int q, int w, int G, int W, int T, int R, int Gs, int kp, int* tile,
+                                        int* kb, int* ke) {
+  if (q < W) {
+    *tile = q * G + w;
+    *kb = 0;
+    *ke = 2 * kp;
+    return true;
+  }
+  if (R == 0 || w >= Gs) return false;
+  const int64_t S = (int64_t)R * kp;
+  const int64_t b = sk_range_begin(w, S, Gs), e = sk_range_begin(w + 1, S, Gs);
+  const int64_t s = b / kp + (q - W);
+  if (b >= e || s * kp >= e) return false; // empty range (only if Gs > S), or past its end
+  const int64_t lo = b > s * kp ? b : s * kp;
+  const int64_t hi = e < (s + 1) * kp ? e : (s + 1) * kp;
+  *tile = (T - R) + (int)s;
+  *kb = (int)(2 * (lo - s * kp));
+  *ke = (int)(2 * (hi - s * kp));
+  return true;
+}
+
+// The same unit sequence, walked incrementally: the 64-bit divisions happen
+// once per workgroup (init); next() then costs a few 32-bit operations, so
+// a kernel can resolve units inside its k-loop. A workgroup's tail range
+// is at most ceil(S/Gs) pairs, which the host keeps below 2^30.
+struct SkWalker {
+  int q, W, G, w, tail0, kp; // unit index; whole waves; grid; workgroup; first tail tile id; pairs per tile
+  int s, off, rem;           // next tail tile index, first pair in it, pairs left in the range
+  __host__ __device__ void init(int w_, int G_, int W_, int T, int R, int Gs, int kp_) {
+    q = 0;
+    W = W_;
+    G = G_;
+    w = w_;
+    kp = kp_;
+    tail0 = T - R;
+    s = off = rem = 0;
+    if (R > 0 && w < Gs) {
+      const int64_t S = (int64_t)R * kp;
+      const int64_t b = sk_range_begin(w, S, Gs), e = sk_range_begin(w + 1, S, Gs);
+      s = (int)(b / kp);
+      off = (int)(b - (int64_t)s * kp);
+      rem = (int)(e - b);
+    }
+  }
+  // Next unit: tile and k-step range [kb, ke); false when none is left.
+  __host__ __device__ bool next(int* tile, int* kb, int* ke) {
+    if (q < W) {
+      *tile = q * G + w;
+      *kb = 0;
+      *ke = 2 * kp;
+      ++q;
+      return true;
+    }
+    if (rem <= 0) return false;
+    const int n = kp - off < rem ? kp - off : rem;
+    *tile = tail0 + s;
+    *kb = 2 * off;
+    *ke = 2 * (off + n);
+    rem -= n;
+    off = 0;
+    ++s;
+    ++q;
+    return true;
+  }
+};
 
 // ------------------------------------------------ buffer loads into LDS
 // gfx9 buffer resource word 3 for raw (untyped) dword access.

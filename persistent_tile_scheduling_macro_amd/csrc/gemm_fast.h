@@ -42,13 +42,16 @@
 // each stage as soon as its fragments are in registers, measured slower on
 // this part: the extra barrier costs more than the earlier copies buy.)
 //
-// All three scheduling modes run this one body over the flattened sequence
-// of (tile, k-step) pairs their scheduler produces. Copies cross tile
+// All scheduling modes run this one body over the flattened sequence of
+// (tile, k-step) pairs their scheduler produces. Copies cross tile
 // boundaries freely, so in the persistent modes the next tile's first copy
 // is in flight while the current tile's epilogue converts and stores C --
 // the pipelining across output tiles the Triton persistent-matmul issue
 // ("Describe the issue") expected persistence to buy. In the
-// non-persistent mode a workgroup owns one tile.
+// non-persistent mode a workgroup owns one tile. In the stream-K mode a
+// work unit is a k-range of a tile (a whole tile in the first waves, a
+// piece of one at the tail); pieces store fp32 partial tiles that
+// sk_fixup_kernel adds up.
 //
 // LDS layouts use 16-byte chunks, swizzled so that the fragment reads are
 // bank-conflict-free on gfx950 (measured: 64 banks; ds_read_b128 serves
@@ -286,6 +289,19 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, 2) gemm_fast_kernel(Par
     }
   };
 
+  // stream-K: the producer and the consumer each walk this workgroup's
+  // work units (tile, k-step range); tile T past the last
+  constexpr bool SK = SCHED == kStreamK;
+  SkWalker p_walk, c_walk;
+  if constexpr (SK) {
+    p_walk.init((int)blockIdx.x, G, p.sk_waves, T, p.sk_tiles, p.sk_groups, nk >> 1);
+    c_walk = p_walk;
+  }
+  auto next_unit = [&](SkWalker& wk, int* kb, int* ke) __attribute__((always_inline)) -> int {
+    int t;
+    return wk.next(&t, kb, ke) ? t : T;
+  };
+
   // ---- producer: the copy of step `issued` ----------------------------------
   // begin_copy() resolves the step's tile and k and builds the buffer
   // resources; copy_part<J>() issues its J-th 1 KiB instruction.
@@ -297,14 +313,28 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, 2) gemm_fast_kernel(Par
   bool p_kval = false;
   int p_mrem = 0, p_krem = 0, p_nrem = 0;
   const uint32_t a_base = (uint32_t)a_row0 * (uint32_t)lda + 16u * (uint32_t)a_chunk;
+  int p_kt = 0, p_ke = 0; // stream-K: next step, end of the unit's k-step range
   auto begin_copy = [&]() __attribute__((always_inline)) {
     if (p_done) return;
-    const int q = issued / nk, kt = issued - q * nk;
-    if (kt == 0) {
-      p_tile = tile_of(q);
-      if (p_tile >= T) {
-        p_done = true;
-        return;
+    int kt;
+    if constexpr (SK) {
+      if (p_kt == p_ke) {
+        p_tile = next_unit(p_walk, &p_kt, &p_ke);
+        if (p_tile >= T) {
+          p_done = true;
+          return;
+        }
+      }
+      kt = p_kt++;
+    } else {
+      const int q = issued / nk;
+      kt = issued - q * nk;
+      if (kt == 0) {
+        p_tile = tile_of(q);
+        if (p_tile >= T) {
+          p_done = true;
+          return;
+        }
       }
     }
     int pm, pn;
@@ -430,6 +460,26 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, 2) gemm_fast_kernel(Par
     }
   };
 
+  // ---- stream-K: store the fp32 partial tile of a piece ---------------------
+  // Workspace slot `slot` holds a BM x BN fp32 tile, row-major; each lane
+  // writes its accumulator blocks at the rows and columns the epilogue
+  // would give them in C.
+  auto store_partial = [&](int slot) __attribute__((always_inline)) {
+    acc_drain();
+    float* base = p.work + (int64_t)slot * (BM * BN);
+    const int r0 = wm * WTM + s16;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      float* row = base + (r0 + mb * 16) * BN + wn * 64;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int col = ES == 2 ? 32 * (nb >> 1) + 8 * g + 4 * ((nb & 1) ^ (g & 1)) : nb * 16 + 4 * g;
+        *reinterpret_cast<floatx4_t*>(row + col) = acc_read(acc[mb][nb]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
   // ---- one k-step on stage C --------------------------------------------------
   int cs = 0; // consumer step
   bool has_next = true;
@@ -524,6 +574,12 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, 2) gemm_fast_kernel(Par
       if (tile_of(0) >= T) return;
     }
   }
+  int c_kb = 0, c_ke = nk; // k-step range of the consumer's unit
+  int c_tile = 0;
+  if constexpr (SK) {
+    c_tile = next_unit(c_walk, &c_kb, &c_ke);
+    if (c_tile >= T) return; // a workgroup without work units (none are launched so; kept as a guard)
+  }
   copy_whole(I0{}); // step 0 into stage 0
   if constexpr (KSUB == 2) {
     copy_whole(I1{}); // step 1 into stage 1 (nk >= 2: same tile)
@@ -535,10 +591,10 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, 2) gemm_fast_kernel(Par
     for (int mb = 0; mb < MB; ++mb) read_a_frag(I0{}, sA0, 0, mb);
   }
   int c_q = 0; // consumer tile sequence number
-  int c_tile = tile_of(0);
+  if constexpr (!SK) c_tile = tile_of(0);
   for (;;) {
     zero_acc();
-    for (int kt = 0; kt < nk; kt += 2) {
+    for (int kt = c_kb; kt < c_ke; kt += 2) {
       step(I0{});
       step(I1{});
     }
@@ -551,12 +607,61 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, 2) gemm_fast_kernel(Par
         claim_live = claimed < T;
       }
     }
-    epilogue(c_tile);
+    if (SK && (c_kb != 0 || c_ke != nk))
+      store_partial((int)blockIdx.x + c_tile - (T - p.sk_tiles));
+    else
+      epilogue(c_tile);
     if constexpr (CLAIMS) {
       if (tid == 0) s_ring[(c_q + 2) & 7] = claimed;
     }
     if (!has_next) break;
-    c_tile = tile_of(++c_q);
+    if constexpr (SK) c_tile = next_unit(c_walk, &c_kb, &c_ke); else c_tile = tile_of(++c_q);
+  }
+}
+
+// ---- stream-K fix-up ----------------------------------------------------------
+// One launch after the stream-K kernel, on the same stream. Workgroup
+// (s, y) finishes rows y*ROWS .. y*ROWS+ROWS-1 of split tile s: it adds the
+// tile's partials slot by slot in k order (workgroups w0..w1 of the split
+// in ascending order, so every run adds the same values in the same
+// order), rounds the sum to nearest even and stores it. Each thread covers
+// eight consecutive columns of one row: two 16-byte partial loads per slot
+// and one 16-byte store. A tile that one workgroup computed whole (w0 ==
+// w1) was stored by that workgroup and is skipped.
+template <int DT, int CFG>
+__global__ void __launch_bounds__(256) sk_fixup_kernel(Params p) {
+  constexpr int BM = Tile<CFG>::BM, BN = Tile<CFG>::BN;
+  constexpr int ES = Traits<DT>::esize, BK = block_k(ES);
+  constexpr int TPR = BN / 8;       // threads per row
+  constexpr int ROWS = 256 / TPR;   // rows per workgroup
+  typedef typename Traits<DT>::out_t out_t;
+  const int s = blockIdx.x;
+  if (s >= p.sk_tiles) return;
+  const int kp = (((p.K + BK - 1) / BK + 1) & ~1) >> 1;
+  const int64_t S = (int64_t)p.sk_tiles * kp;
+  const int w0 = sk_owner((int64_t)s * kp, S, p.sk_groups);
+  const int w1 = sk_owner((int64_t)(s + 1) * kp - 1, S, p.sk_groups);
+  if (w0 == w1) return;
+  const int tile = p.T - p.sk_tiles + s;
+  int pm, pn;
+  tile_coords(tile, p, &pm, &pn);
+  const int r = blockIdx.y * ROWS + (int)threadIdx.x / TPR;
+  const int c = ((int)threadIdx.x % TPR) * 8;
+  const int m = pm * BM + r, n = pn * BN + c;
+  if (r < BM && m < p.M && n < p.N) { // N is a multiple of 8: the 8 columns are all inside
+    const float* src = p.work + (int64_t)(w0 + s) * (BM * BN) + r * BN + c;
+    floatx4_t lo = *reinterpret_cast<const floatx4_t*>(src);
+    floatx4_t hi = *reinterpret_cast<const floatx4_t*>(src + 4);
+    for (int w = w0 + 1; w <= w1; ++w) {
+      src += (int64_t)BM * BN;
+      lo += *reinterpret_cast<const floatx4_t*>(src);
+      hi += *reinterpret_cast<const floatx4_t*>(src + 4);
+    }
+    store8(reinterpret_cast<out_t*>(p.C) + (int64_t)m * p.N + n, lo, hi, false);
+  }
+  if (blockIdx.y == 0 && threadIdx.x == 0) {
+    if (p.visits) atomicAdd(p.visits + tile, 1);
+    if (p.owner) p.owner[tile] = -1 - s; // stored by the fix-up, not by a workgroup of the GEMM grid
   }
 }
 

@@ -16,6 +16,11 @@ kernel_fn pick_kernel_f16(int sched, int body);
 kernel_fn pick_kernel_bf16(int sched, int body);
 kernel_fn pick_kernel_f8(int sched, int body);
 
+// The stream-K fix-up kernel of a fast tile body (nullptr for the generic body).
+kernel_fn pick_fixup_f16(int body);
+kernel_fn pick_fixup_bf16(int body);
+kernel_fn pick_fixup_f8(int body);
+
 // K == 0: C = 0 (an empty sum). n = M * N output elements.
 void launch_fill_zero(void* C, int64_t n, hipStream_t stream);
 

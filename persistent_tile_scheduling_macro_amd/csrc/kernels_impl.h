@@ -13,7 +13,8 @@ kernel_fn pick_body(int body) {
   switch (body) {
     case kBodyTile256: return fast::gemm_fast_kernel<DT, SCHED, fast::kTile256>;
     case kBodyTile128: return fast::gemm_fast_kernel<DT, SCHED, fast::kTile128>;
-    default: return generic::gemm_generic_kernel<DT, SCHED>;
+    default: // the generic body has no stream-K split: it runs that mode as static
+      return generic::gemm_generic_kernel<DT, SCHED == kStreamK ? kStatic : SCHED>;
   }
 }
 
@@ -23,7 +24,17 @@ kernel_fn pick_for_dtype(int sched, int body) {
     case kNonPersistent: return pick_body<DT, kNonPersistent>(body);
     case kStatic: return pick_body<DT, kStatic>(body);
     case kDynamic: return pick_body<DT, kDynamic>(body);
-    default: return pick_body<DT, kCancel>(body);
+    case kCancel: return pick_body<DT, kCancel>(body);
+    default: return pick_body<DT, kStreamK>(body);
+  }
+}
+
+template <int DT>
+kernel_fn pick_fixup_for_dtype(int body) {
+  switch (body) {
+    case kBodyTile256: return fast::sk_fixup_kernel<DT, fast::kTile256>;
+    case kBodyTile128: return fast::sk_fixup_kernel<DT, fast::kTile128>;
+    default: return nullptr;
   }
 }
 

@@ -30,6 +30,11 @@ struct pgemm_ctx {
   int group_m = 4;
   int xcd_remap = 0;
   int tile = PGEMM_TILE_AUTO; // macro-tile choice of the fast kernel
+  // Stream-K: shortest piece, in k-step pairs, a split may cut (tiles with
+  // fewer pairs are not split).
+  int sk_min_pairs = 4;
+  float* work = nullptr; // stream-K partial tiles, grown on demand
+  size_t work_bytes = 0;
   char last_error[512] = {0};
 };
 
@@ -67,6 +72,14 @@ kernel_fn pick_kernel(int dtype, int sched, int body) {
   }
 }
 
+kernel_fn pick_fixup(int dtype, int body) {
+  switch (dtype) {
+    case kF16: return pick_fixup_f16(body);
+    case kBF16: return pick_fixup_bf16(body);
+    default: return pick_fixup_f8(body);
+  }
+}
+
 // Tile body for an aligned problem. Automatic choice: the 256 x 256 tile
 // moves the fewest operand bytes per flop and measured faster whenever it
 // gives every CU a tile (4096^2 to 8200^2, every K); when it would leave CUs
@@ -98,7 +111,38 @@ struct Plan {
   int64_t n_m, n_n, T;
   int occupancy;
   int64_t G;
+  // stream-K split (all zero in the other modes)
+  int sk_waves = 0, sk_tiles = 0, sk_groups = 0, sk_split = 0; // sk_split: tiles cut into pieces
+  size_t work_bytes = 0;
 };
+
+// Stream-K split of a fast launch (the helpers' comment in device_common.h
+// gives the scheme): W = T / G whole-tile waves on G = mult * CUs
+// workgroups, the R = T mod G tail tiles' S = R * kp pairs cut into
+// Gs = min(G, S / min(kp, min_pairs)) ranges. The grid is G when W >= 1,
+// else Gs.
+void plan_streamk(const pgemm_ctx* h, int64_t K, int64_t G_full, Plan* pl) {
+  const int64_t nk = ((K + pl->bk - 1) / pl->bk + 1) & ~(int64_t)1;
+  const int64_t kp = nk / 2;
+  const int64_t W = pl->T / G_full, R = pl->T % G_full;
+  pl->sk_waves = (int)W;
+  pl->sk_tiles = (int)R;
+  int64_t Gs = 0;
+  if (R > 0) {
+    const int64_t S = R * kp;
+    const int64_t minp = std::max<int64_t>(1, std::min<int64_t>(kp, h->sk_min_pairs));
+    Gs = std::max<int64_t>(1, std::min<int64_t>(G_full, S / minp));
+  }
+  pl->sk_groups = (int)Gs;
+  pl->G = W >= 1 ? G_full : Gs;
+  int split = 0;
+  for (int64_t s = 0; s < R; ++s) {
+    const int64_t S = R * kp;
+    if (sk_owner(s * kp, S, (int)Gs) != sk_owner((s + 1) * kp - 1, S, (int)Gs)) ++split;
+  }
+  pl->sk_split = split;
+  pl->work_bytes = split ? (size_t)(Gs + R) * (size_t)pl->bm * (size_t)pl->bn * sizeof(float) : 0;
+}
 
 int plan_launch(pgemm_ctx* h, int64_t M, int64_t N, int64_t K, int dtype, int sched, int grid_multiple,
                 bool fast, Plan* pl) {
@@ -127,11 +171,20 @@ int plan_launch(pgemm_ctx* h, int64_t M, int64_t N, int64_t K, int dtype, int sc
   if (e != hipSuccess) return fail(h, PGEMM_ERR_HIP, "occupancy query: %s", hipGetErrorString(e));
   if (occ < 1) occ = 1;
   pl->occupancy = occ;
+  const int64_t mult = grid_multiple <= 0 ? occ : grid_multiple;
   if (sched == kNonPersistent || sched == kCancel) {
     pl->G = pl->T; // one workgroup per tile (cancel-and-reuse: late ones find none left)
+  } else if (sched == kStreamK && fast) {
+    // pair positions (< T * kp) and the owner arithmetic stay inside int64
+    const int64_t kp = (((K + pl->bk - 1) / pl->bk + 1) & ~(int64_t)1) / 2;
+    if (pl->T * kp >= ((int64_t)1 << 40) || mult * h->cus >= ((int64_t)1 << 20))
+      return fail(h, PGEMM_ERR_UNSUPPORTED, "stream-K split too large (tiles x k-steps or grid)");
+    plan_streamk(h, K, mult * h->cus, pl);
+    // a workgroup's tail range (in k-step pairs) must fit the kernel's 32-bit walker
+    if (pl->sk_tiles && ((int64_t)pl->sk_tiles * kp + pl->sk_groups - 1) / pl->sk_groups >= ((int64_t)1 << 30))
+      return fail(h, PGEMM_ERR_UNSUPPORTED, "stream-K range per workgroup too long");
   } else {
-    const int64_t mult = grid_multiple <= 0 ? occ : grid_multiple;
-    pl->G = std::min<int64_t>(mult * h->cus, pl->T);
+    pl->G = std::min<int64_t>(mult * h->cus, pl->T); // static, dynamic; stream-K on the generic body
   }
   return PGEMM_OK;
 }
@@ -144,7 +197,7 @@ int check_common(pgemm_ctx* h, int64_t M, int64_t N, int64_t K, int dtype, int s
   if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX)
     return fail(h, PGEMM_ERR_UNSUPPORTED, "sizes must be below 2^31");
   if (dtype < PGEMM_F16 || dtype > PGEMM_F8E4M3_BF16) return fail(h, PGEMM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
-  if (sched < PGEMM_SCHED_NONPERSISTENT || sched > PGEMM_SCHED_CANCEL)
+  if (sched < PGEMM_SCHED_NONPERSISTENT || sched > PGEMM_SCHED_STREAMK)
     return fail(h, PGEMM_ERR_INVALID_ARG, "unknown sched_mode %d", sched);
   return PGEMM_OK;
 }
@@ -177,6 +230,7 @@ int pgemm_create(pgemm_handle_t* out, int device) {
   }
   if (const char* g = getenv("PGEMM_GROUP_M")) h->group_m = std::max(1, atoi(g));
   if (const char* x = getenv("PGEMM_XCD_REMAP")) h->xcd_remap = atoi(x) != 0;
+  if (const char* m = getenv("PGEMM_SK_MIN_PAIRS")) h->sk_min_pairs = std::max(1, atoi(m));
   if (const char* t = getenv("PGEMM_TILE")) {
     const int v = atoi(t);
     h->tile = v == 256 ? PGEMM_TILE_256 : v == 128 ? PGEMM_TILE_128 : PGEMM_TILE_AUTO;
@@ -231,10 +285,68 @@ int pgemm_run(pgemm_handle_t h, const void* A, const void* B, void* C, int64_t M
   p.counter = h->counter;
   p.visits = h->visits;
   p.owner = h->owner;
-  kernel_fn k = pick_kernel(dtype, sched_mode, pl.body);
-  hipLaunchKernelGGL(k, dim3((unsigned)pl.G), dim3(pl.threads), 0, h->stream, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(h, PGEMM_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+  p.sk_waves = pl.sk_waves;
+  p.sk_tiles = pl.sk_tiles;
+  p.sk_groups = pl.sk_groups;
+  p.work = nullptr;
+  if (pl.work_bytes) {
+    if (pl.work_bytes > h->work_bytes) {
+      // grow the workspace: wait for launches that may still use the old one
+      if (hipStreamSynchronize(h->stream) != hipSuccess) return fail(h, PGEMM_ERR_HIP, "stream synchronize failed");
+      if (h->work) hipFree(h->work);
+      h->work = nullptr;
+      h->work_bytes = 0;
+      if (hipMalloc(&h->work, pl.work_bytes) != hipSuccess) {
+        h->work = nullptr;
+        (void)hipGetLastError();
+        return fail(h, PGEMM_ERR_OOM, "stream-K workspace of %zu bytes", pl.work_bytes);
+      }
+      h->work_bytes = pl.work_bytes;
+    }
+    p.work = h->work;
+  }
+  if (sched_mode != kStreamK || !pl.fast) {
+    kernel_fn k = pick_kernel(dtype, sched_mode, pl.body);
+    hipLaunchKernelGGL(k, dim3((unsigned)pl.G), dim3(pl.threads), 0, h->stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(h, PGEMM_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+    return PGEMM_OK;
+  }
+  // Stream-K as up to three launches on the stream: (1) the W whole waves, by
+  // the static kernel over the first W*G tiles of the tile order (its tile
+  // sequence, unchanged: tile coordinates do not depend on T, and the XCD
+  // remap's chunk, the CU count, divides W*G); (2) the R tail tiles' split,
+  // by the stream-K kernel on its own grid of Gs workgroups; (3) the fix-up
+  // of split tiles. Keeping the whole waves in the static kernel keeps them
+  // at its speed: the stream-K kernel's partial-tile stores make the compiler
+  // add a wait for every outstanding global->LDS copy inside its k-loop
+  // (measured 8% slower at 8192^3).
+  if (pl.sk_waves > 0) {
+    Params pd = p;
+    pd.T = (int)(pl.T - pl.sk_tiles); // W * G
+    pd.sk_waves = pd.sk_tiles = pd.sk_groups = 0;
+    pd.work = nullptr;
+    hipLaunchKernelGGL(pick_kernel(dtype, kStatic, pl.body), dim3((unsigned)pl.G), dim3(pl.threads), 0, h->stream, pd);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(h, PGEMM_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+  }
+  if (pl.sk_tiles > 0) {
+    Params ps = p;
+    ps.sk_waves = 0;
+    ps.G = pl.sk_groups;
+    hipLaunchKernelGGL(pick_kernel(dtype, kStreamK, pl.body), dim3((unsigned)pl.sk_groups), dim3(pl.threads), 0,
+                       h->stream, ps);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(h, PGEMM_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+    if (pl.sk_split) {
+      // 256 threads cover 8 columns each: 256 / (bn / 8) rows per workgroup
+      const unsigned rows_per_wg = 256u / (unsigned)(pl.bn / 8);
+      hipLaunchKernelGGL(pick_fixup(dtype, pl.body), dim3((unsigned)pl.sk_tiles, (unsigned)pl.bm / rows_per_wg),
+                         dim3(256), 0, h->stream, ps);
+      e = hipGetLastError();
+      if (e != hipSuccess) return fail(h, PGEMM_ERR_HIP, "fix-up launch: %s", hipGetErrorString(e));
+    }
+  }
   return PGEMM_OK;
 }
 
@@ -244,6 +356,7 @@ int pgemm_destroy(pgemm_handle_t h) {
   if (hipSetDevice(h->device) != hipSuccess) rc = PGEMM_ERR_HIP;
   if (hipStreamSynchronize(h->stream) != hipSuccess) rc = PGEMM_ERR_HIP;
   if (hipFree(h->counter) != hipSuccess) rc = PGEMM_ERR_HIP;
+  if (h->work && hipFree(h->work) != hipSuccess) rc = PGEMM_ERR_HIP;
   delete h;
   return rc;
 }
@@ -292,6 +405,22 @@ int pgemm_query_launch(pgemm_handle_t h, int64_t M, int64_t N, int64_t K, int dt
   if (bn) *bn = pl.bn;
   if (bk) *bk = pl.bk;
   if (fast_path) *fast_path = pl.fast ? 1 : 0;
+  return PGEMM_OK;
+}
+
+int pgemm_query_streamk(pgemm_handle_t h, int64_t M, int64_t N, int64_t K, int dtype, int grid_multiple,
+                        int* whole_tiles, int* split_tiles, int* split_groups, int* pieces_split,
+                        int64_t* workspace_bytes) {
+  int rc = check_common(h, M, N, K, dtype, PGEMM_SCHED_STREAMK);
+  if (rc != PGEMM_OK) return rc;
+  Plan pl;
+  rc = plan_launch(h, M, N, K, dtype, PGEMM_SCHED_STREAMK, grid_multiple, sizes_fast(dtype, N, K), &pl);
+  if (rc != PGEMM_OK) return rc;
+  if (whole_tiles) *whole_tiles = (int)(pl.T - pl.sk_tiles);
+  if (split_tiles) *split_tiles = pl.sk_tiles;
+  if (split_groups) *split_groups = pl.sk_groups;
+  if (pieces_split) *pieces_split = pl.sk_split;
+  if (workspace_bytes) *workspace_bytes = (int64_t)pl.work_bytes;
   return PGEMM_OK;
 }
 

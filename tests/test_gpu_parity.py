@@ -7,7 +7,9 @@ Checks, per case (see the oracle's header for what is computed):
   output type (every partial sum is an integer below 2^24, exact in fp32 in
   any order);
 * tile-visit counter: every output tile written exactly once;
-* C bitwise identical across the four scheduling modes (one tile body).
+* C bitwise identical across the four tile-scheduling modes (one tile
+  body); the stream-K mode, which adds split tiles' partial sums, is held
+  to the oracle bound (and to bit-exactness on small integers) instead.
 
 Every case runs with each macro-tile configuration of the fast kernel
 (256 x 256 and 128 x 128), selected explicitly through the C ABI.
@@ -24,7 +26,8 @@ pytestmark = pytest.mark.gpu
 DT = {"f16": 0, "bf16": 1, "e4m3fn": 2}
 OUT = {"f16": ("f16", torch.float16), "bf16": ("bf16", torch.bfloat16), "e4m3fn": ("bf16", torch.bfloat16)}
 TOL = {"f16": 2e-3, "bf16": 2e-3, "e4m3fn": 1e-2}
-MODES = [0, 1, 2, 3]  # non-persistent, static, dynamic, cancel-and-reuse
+MODES = [0, 1, 2, 3, 4]  # non-persistent, static, dynamic, cancel-and-reuse, stream-K
+SAME_BITS = [0, 1, 2, 3]  # modes that run every tile whole: C bitwise identical
 TILES = {"t256": 1, "t128": 2}  # PGEMM_TILE_256, PGEMM_TILE_128
 
 
@@ -81,7 +84,8 @@ def test_workload_256_all_modes(pg, handle, dtype):
         assert err <= TOL[dtype], (mode, err)
         assert info["fast_path"] == 1 and info["tiles"] == (256 // info["bm"]) ** 2
         assert np.array_equal(v, np.ones_like(v)), v
-        outs.append(c)
+        if mode in SAME_BITS:
+            outs.append(c)
     for o in outs[1:]:
         assert np.array_equal(outs[0], o)
 
@@ -120,7 +124,8 @@ def test_uniform_parity(pg, handle, dtype, shape):
         err = oracle.normwise_error(c, OUT[dtype][0], ref)
         assert err <= TOL[dtype], (mode, err)
         assert np.array_equal(v[:info["tiles"]], np.ones(info["tiles"], np.int32))
-        outs.append(c)
+        if mode in SAME_BITS:
+            outs.append(c)
     for o in outs[1:]:
         assert np.array_equal(outs[0], o)
 
@@ -214,7 +219,7 @@ def test_invalid_arguments(pg, handle):
     with pytest.raises(pg.PgemmError):
         pg.pgemm_run(handle, A, A, A, 4, 8, 8, 7, 1, 0)
     with pytest.raises(pg.PgemmError):
-        pg.pgemm_run(handle, A, A, A, 4, 8, 8, 0, 4, 0)
+        pg.pgemm_run(handle, A, A, A, 4, 8, 8, 0, 5, 0)
     with pytest.raises(pg.PgemmError):
         pg.pgemm_run(handle, 0, A, A, 4, 8, 8, 0, 1, 0)
     small = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -261,7 +266,7 @@ def test_graph_capture_and_replay(pg):
     scheduling mode is replayed several times with eager work in between;
     every replay's C is bit-exact and the counter reads 0 after each."""
     dev = torch.device("cuda:0")
-    M, N, K = 1024, 768, 320
+    M, N, K = 1024, 768, 1024  # 48 tiles of 128^2: stream-K splits each in two (a fix-up node too)
     A, B = si.operands(M, N, K, "f16", "small_int", workload=13)
     want = oracle.round_to(oracle.gemm(si.bits(A), si.bits(B), "f16"), "f16")
     Ad, Bd = A.to(dev), B.to(dev)
@@ -269,6 +274,8 @@ def test_graph_capture_and_replay(pg):
     h = pg.pgemm_create(0)
     try:
         pg.pgemm_set_tile_config(h, pg.PGEMM_TILE_128)
+        for C, mode in zip(Cs, MODES):  # eager runs first: any stream-K workspace exists before capture
+            pg.pgemm_run(h, Ad, Bd, C, M, N, K, 0, mode, 0)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):

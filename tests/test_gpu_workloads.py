@@ -12,7 +12,8 @@ and 64 further seeded rows, all N columns each. Per launch:
 * tile-visit counter all ones (every tile of the full C written once), which
   covers the rows that sampling misses;
 * C bitwise identical to the first mode's C (checked on the device, whole
-  matrix).
+  matrix) for the modes that run every tile whole; the stream-K mode, whose
+  split tiles add fp32 partials, is checked against a rerun of itself.
 
 Inputs are drawn exactly as the benchmark draws them: once at the largest K
 of the workload, then the leading K columns of A and rows of B.
@@ -37,6 +38,7 @@ K_SUBSET = {
     "sweep8k": [256, 2304, 8192],
     "fp8": [8192],
     "tail": [4000, 6144, 8200],
+    "fewtiles": [2048, 32768],
     "square8k": [8192],
 }
 
@@ -101,7 +103,13 @@ def test_workload_sampled_parity(pg, handle, workload):
                 err = oracle.normwise_error(c_rows, OUT[dtype][0], ref)
                 assert err <= TOL[dtype], (mode, gm, err)
                 cb = C.view(torch.int16)
-                if first is None:
+                if mode == 4:  # stream-K: deterministic, but its own bits
+                    C2 = torch.empty_like(C)
+                    pg.pgemm_run(handle, Ad, Bd, C2, m, n, K, DT[dtype], mode, gm)
+                    torch.cuda.synchronize()
+                    assert torch.equal(C2.view(torch.int16), cb), (mode, gm, "stream-K rerun differs")
+                    del C2
+                elif first is None:
                     first = cb.clone()
                 else:
                     assert torch.equal(cb, first), (mode, gm, "C differs bitwise from the first mode")
