@@ -104,3 +104,20 @@ def test_cancel_mode_is_accepted_and_unknown_modes_are_not(pg):
     with pytest.raises(pg.PgemmError) as e:
         pg.pgemm_run(None, 0, 0, 0, 1, 1, 1, 0, 3, 0)
     assert e.value.status == pg.PGEMM_ERR_INVALID_ARG  # null handle, not an unknown mode
+
+
+def test_query_entry_points_reject_a_null_handle(pg):
+    """The planning queries need a handle (its CU count); without one they fail cleanly."""
+    with pytest.raises(pg.PgemmError) as e:
+        pg.pgemm_query_launch(None, 256, 256, 256, 0, 1, 0)
+    assert e.value.status == pg.PGEMM_ERR_INVALID_ARG
+    with pytest.raises(pg.PgemmError) as e:
+        pg.pgemm_query_streamk(None, 256, 256, 256, 0, 0)
+    assert e.value.status == pg.PGEMM_ERR_INVALID_ARG
+
+
+def test_streamk_mode_constant_matches_the_header(pg):
+    text = open(HEADER).read()
+    m = re.search(r"PGEMM_SCHED_STREAMK\s*=\s*(\d+)", text)
+    assert m and int(m.group(1)) == pg.PGEMM_SCHED_STREAMK == 4
+    assert pg.SCHED_NAMES["streamk"] == 4
