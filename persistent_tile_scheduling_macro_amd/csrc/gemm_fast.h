@@ -16,15 +16,20 @@
 // staging) into a two-stage ring, so the copy of step s+1 overlaps the
 // MFMAs of step s (the copy/compute overlap of the persistent-kernel forum
 // thread, first answer). Both configurations copy 4 + 4 KiB-sized
-// instructions per thread per step.
+// instructions per thread per step (the body is written for waves of 64 or
+// 128 columns and any even copy count).
 //
 // Why this shape on gfx950 (measured on the part, not taken from the
-// pages): the CU's global -> LDS path moves about 30 B/clk, while a 256 x
-// 256 tile's MFMAs consume 32 B/clk of operands at full rate, so the
-// kernel is bound by that path; copies and MFMAs issued by the same wave
-// overlap poorly, two waves per SIMD overlap them much better; and copy
-// rows must be whole 128-byte lines (half-line rows cut the path's
-// throughput at full occupancy).
+// pages): a 256 x 256 tile's MFMAs need 32 B/clk of operand copies at full
+// rate, which the CU's global -> LDS path (about 46 B/clk for whole-line
+// copies) sustains. What binds is the LDS: it serves the fragment reads
+// (256 B/clk for 16-byte reads, 172 B/clk for the transposing reads) and
+// takes the copies' writes, and at this kernel's mix its read throughput
+// falls to about 110 B/clk, near the 96 B/clk the fragment reads need at
+// full MFMA rate. Two waves per SIMD overlap that with the MFMAs far
+// better than one: four waves of 128 x 128, which read a third less from
+// LDS, measured 9-20% slower. Copy rows must be whole 128-byte lines
+// (half-line rows cut the copy path's throughput at full occupancy).
 //
 // Step s on stage c = s mod 2 (16-bit: two MFMA k-groups per step):
 //   1. MFMAs of k-group 0 (fragments read during step s-1) while the
@@ -96,11 +101,23 @@ struct Tile;
 template <>
 struct Tile<kTile256> {
   static constexpr int BM = 256, BN = 256, WAVES = 8, WGM = 2, WGN = 4;
+  static constexpr int MIN_WAVES_PER_SIMD = 2;
 };
 template <>
 struct Tile<kTile128> {
   static constexpr int BM = 128, BN = 128, WAVES = 4, WGM = 2, WGN = 2;
+  static constexpr int MIN_WAVES_PER_SIMD = 2; // two workgroups per CU
 };
+
+// Compile-time loop: f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>).
+template <class F, int... I>
+__device__ __attribute__((always_inline)) inline void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __attribute__((always_inline)) inline void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // Swizzle of B's LDS rows: row k's chunk c is stored at chunk c ^ b_swz(k).
 template <int ES, int B_ROW>
@@ -158,13 +175,15 @@ __device__ inline typename Frag<DT>::t read_a(const uint8_t* lo, const uint8_t* 
 }
 
 template <int DT, int SCHED, int CFG>
-__global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, 2) gemm_fast_kernel(Params p) {
+__global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, Tile<CFG>::MIN_WAVES_PER_SIMD) gemm_fast_kernel(Params p) {
   constexpr int BM = Tile<CFG>::BM, BN = Tile<CFG>::BN;
   constexpr int WAVES = Tile<CFG>::WAVES, THREADS = WAVES * 64;
   constexpr int WGN = Tile<CFG>::WGN;             // waves along n
   constexpr int WTM = BM / Tile<CFG>::WGM;        // rows of a wave's sub-tile
   constexpr int MB = WTM / 16;                    // 16-row MFMA blocks per wave (8 or 4)
-  static_assert(BN / WGN == 64, "each wave owns 64 columns = 4 MFMA blocks");
+  constexpr int WN = BN / WGN;                    // columns of a wave's sub-tile
+  constexpr int NB = WN / 16;                     // 16-column MFMA blocks per wave (4 or 8)
+  static_assert(NB == 4 || NB == 8, "a wave owns 64 or 128 columns");
   constexpr int ES = Traits<DT>::esize;
   constexpr int BK = block_k(ES);                // k elements per step
   constexpr int KSUB = BK / Traits<DT>::kgroup;  // MFMA k-groups per step (2 or 1)
@@ -176,7 +195,9 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, 2) gemm_fast_kernel(Par
   constexpr int B_RPI = 1024 / B_ROW;            // B rows per 1 KiB copy instruction
   constexpr int LA = A_BYTES / (THREADS * 16), LB = B_BYTES / (THREADS * 16);
   constexpr int L = LA + LB;                     // copy instructions per thread per step
-  static_assert(LA == 4 && LB == 4, "copy split assumes 4 + 4 instructions per step");
+  static_assert(LA * THREADS * 16 == A_BYTES && LB * THREADS * 16 == B_BYTES && (L & 1) == 0,
+                "each thread copies whole 16-byte chunks, in pairs of instructions");
+  static_assert(L / 2 <= MB, "the fp8 step issues one copy pair per MFMA row");
   static_assert(MB <= 8, "fragment arrays sized for at most 8 row blocks");
   typedef typename Traits<DT>::out_t out_t;
   typedef typename Frag<DT>::t frag_t;
@@ -225,8 +246,9 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, 2) gemm_fast_kernel(Par
     a_chunk = (lane & 7) ^ (((r >> 1) & 1) | (r & 4));
   }
   const int b_row0 = B_RPI * wave + lane / B_CPR; // + B_RPI*WAVES j
+  // Instruction JB adds B_RPI*WAVES*JB rows, which only sets row bits above those of b_row0;
+  // the swizzle is a sum of single-bit terms, so its value for the sum is the XOR of the two.
   const int b_chunk0 = (lane % B_CPR) ^ b_swz<ES, B_ROW>(b_row0);
-  const int b_chunk1 = (lane % B_CPR) ^ b_swz<ES, B_ROW>(b_row0 + B_RPI * WAVES);
 
   // ---- per-lane constants of the fragment reads ----------------------------
   const int g = lane >> 4, s16 = lane & 15;
@@ -245,9 +267,9 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, 2) gemm_fast_kernel(Par
       }
     }
   }
-  int b_off[4];
+  int b_off[NB];
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
+  for (int nb = 0; nb < NB; ++nb) {
     // the swizzle is the same for every row this lane reads from here
     // (+4 and +32 rows for 16-bit, +8/+16/+24 for fp8)
     if constexpr (ES == 2) {
@@ -255,11 +277,11 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, 2) gemm_fast_kernel(Par
       // column 32*(nb/2) + 8q + 4*((nb + q) & 1) (permuted order)
       const int k = 8 * g + (s16 >> 2);
       const int q = s16 & 3;
-      const int Lc = wn * 8 + 4 * (nb >> 1) + q;
+      const int Lc = wn * (WN / 8) + 4 * (nb >> 1) + q;
       b_off[nb] = k * B_ROW + 16 * (Lc ^ b_swz<ES, B_ROW>(k)) + 8 * ((nb + q) & 1);
     } else {
       const int k = 32 * g + (s16 >> 1);
-      const int Lc = wn * 4 + nb;
+      const int Lc = wn * (WN / 16) + nb;
       b_off[nb] = k * B_ROW + 16 * (Lc ^ b_swz<ES, B_ROW>(k)) + 8 * (s16 & 1);
     }
   }
@@ -361,7 +383,7 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, 2) gemm_fast_kernel(Par
     } else {
       constexpr int JB = J - LA;
       const int row = b_row0 + B_RPI * WAVES * JB;
-      const int Lc = (JB & 1) ? b_chunk1 : b_chunk0;
+      const int Lc = b_chunk0 ^ b_swz<ES, B_ROW>(B_RPI * WAVES * JB);
       const bool ok = (row < p_krem) & (16 * Lc < p_nrem);
       const uint32_t off = ok ? (uint32_t)row * (uint32_t)ldb + 16u * (uint32_t)Lc : kOOB;
       load16_to_lds(rb, sB + (wave + WAVES * JB) * 1024, off);
@@ -375,13 +397,13 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, 2) gemm_fast_kernel(Par
   };
 
   // ---- accumulators and fragments -------------------------------------------
-  floatx4_t acc[MB][4];
-  frag_t af[2][MB], bf[2][4];
+  floatx4_t acc[MB][NB];
+  frag_t af[2][MB], bf[2][NB];
   auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < NB; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
     acc_drain(); // accvgpr writes -> MFMA srcC reads
   };
   auto read_a_frag = [&](auto f, const uint8_t* sA, int kk, int mb) __attribute__((always_inline)) {
@@ -395,7 +417,7 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, 2) gemm_fast_kernel(Par
   auto mfma_row = [&](auto f, int mb) __attribute__((always_inline)) {
     constexpr int F = decltype(f)::value;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) mfma_acc(acc[mb][nb], bf[F][nb], af[F][mb]);
+    for (int nb = 0; nb < NB; ++nb) mfma_acc(acc[mb][nb], bf[F][nb], af[F][mb]);
   };
 
   // ---- epilogue: round to the output type and store one tile ---------------
@@ -411,15 +433,16 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, 2) gemm_fast_kernel(Par
       // of 8, so each 16-byte store is wholly inside or outside C. Interior
       // tiles (the uniform common case) store without masks; the schedule
       // barriers keep each row block's accumulator reads next to its stores.
-      const int ncol8 = pn * BN + wn * 64 + 8 * g;
+      const int ncol8 = pn * BN + wn * WN + 8 * g;
       const bool odd = (g & 1) != 0;
       out_t* crow = C + (int64_t)mrow * ldc + ncol8;
       if ((pm * BM + BM <= M) & (pn * BN + BN <= N)) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           out_t* dst = crow + (int64_t)(16 * mb) * ldc;
-          store8(dst, acc_read(acc[mb][0]), acc_read(acc[mb][1]), odd);
-          store8(dst + 32, acc_read(acc[mb][2]), acc_read(acc[mb][3]), odd);
+#pragma unroll
+          for (int P = 0; P < NB / 2; ++P)
+            store8(dst + 32 * P, acc_read(acc[mb][2 * P]), acc_read(acc[mb][2 * P + 1]), odd);
           __builtin_amdgcn_sched_barrier(0);
         }
       } else {
@@ -427,20 +450,21 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, 2) gemm_fast_kernel(Par
         for (int mb = 0; mb < MB; ++mb) {
           if (mrow + mb * 16 < M) {
             out_t* dst = crow + (int64_t)(16 * mb) * ldc;
-            if (ncol8 < N) store8(dst, acc_read(acc[mb][0]), acc_read(acc[mb][1]), odd);
-            if (ncol8 + 32 < N) store8(dst + 32, acc_read(acc[mb][2]), acc_read(acc[mb][3]), odd);
+#pragma unroll
+            for (int P = 0; P < NB / 2; ++P)
+              if (ncol8 + 32 * P < N) store8(dst + 32 * P, acc_read(acc[mb][2 * P]), acc_read(acc[mb][2 * P + 1]), odd);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
       }
     } else {
-      const int ncol = pn * BN + wn * 64 + 4 * g;
+      const int ncol = pn * BN + wn * WN + 4 * g;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         const int m = mrow + mb * 16;
         if (m < M) {
 #pragma unroll
-          for (int nb = 0; nb < 4; ++nb) {
+          for (int nb = 0; nb < NB; ++nb) {
             const int n = ncol + nb * 16;
             out_t* dst = C + (int64_t)m * ldc + n;
             if (n + 3 < N) {
@@ -470,9 +494,9 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, 2) gemm_fast_kernel(Par
     const int r0 = wm * WTM + s16;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      float* row = base + (r0 + mb * 16) * BN + wn * 64;
+      float* row = base + (r0 + mb * 16) * BN + wn * WN;
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
+      for (int nb = 0; nb < NB; ++nb) {
         const int col = ES == 2 ? 32 * (nb >> 1) + 8 * g + 4 * ((nb & 1) ^ (g & 1)) : nb * 16 + 4 * g;
         *reinterpret_cast<floatx4_t*>(row + col) = acc_read(acc[mb][nb]);
       }
@@ -494,18 +518,15 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, 2) gemm_fast_kernel(Par
     begin_copy();
     has_next = p_busy;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) read_b_frag(I0{}, sB, 0, nb);
+    for (int nb = 0; nb < NB; ++nb) read_b_frag(I0{}, sB, 0, nb);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) read_a_frag(I0{}, sA, 0, mb);
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      mfma_row(I0{}, mb);
-      if (mb == 0) copy_pair(ICN{}, std::integral_constant<int, 0>{});
-      if (mb == 1) copy_pair(ICN{}, std::integral_constant<int, 1>{});
-      if (mb == 2) copy_pair(ICN{}, std::integral_constant<int, 2>{});
-      if (mb == 3) copy_pair(ICN{}, std::integral_constant<int, 3>{});
+    static_for<MB>([&](auto mbc) __attribute__((always_inline)) {
+      constexpr int MBI = decltype(mbc)::value;
+      mfma_row(I0{}, MBI);
+      if constexpr (MBI < L / 2) copy_pair(ICN{}, std::integral_constant<int, MBI>{});
       __builtin_amdgcn_sched_barrier(0);
-    }
+    });
     ++cs;
   };
   // mid-step variant (16-bit): the barrier sits between the two k-groups.
@@ -522,7 +543,7 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, 2) gemm_fast_kernel(Par
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       mfma_row(I0{}, mb);
-      if (mb < 4) read_b_frag(I1{}, sB, 1, mb);
+      if (mb < NB) read_b_frag(I1{}, sB, 1, mb);
       read_a_frag(I1{}, sA, 1, mb);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -531,15 +552,12 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, 2) gemm_fast_kernel(Par
       wait_vmcnt<0>(); // this wave's copy of step cs+1 (and any older stores) landed
       __syncthreads(); // every wave's; and every wave has read all of stage C
       begin_copy();    // step cs + 2 into stage C
-      copy_pair(cst, std::integral_constant<int, 0>{});
-      copy_pair(cst, std::integral_constant<int, 1>{});
-      copy_pair(cst, std::integral_constant<int, 2>{});
-      copy_pair(cst, std::integral_constant<int, 3>{});
+      static_for<L / 2>([&](auto pc) __attribute__((always_inline)) { copy_pair(cst, pc); });
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       mfma_row(I1{}, mb);
-      if (mb < 4) read_b_frag(I0{}, sBn, 0, mb); // stale but harmless without a next step
+      if (mb < NB) read_b_frag(I0{}, sBn, 0, mb); // stale but harmless without a next step
       read_a_frag(I0{}, sAn, 0, mb);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -552,10 +570,7 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, 2) gemm_fast_kernel(Par
   // ---- the (tile, k-step) pipeline -----------------------------------------
   auto copy_whole = [&](auto c) __attribute__((always_inline)) {
     begin_copy();
-    copy_pair(c, std::integral_constant<int, 0>{});
-    copy_pair(c, std::integral_constant<int, 1>{});
-    copy_pair(c, std::integral_constant<int, 2>{});
-    copy_pair(c, std::integral_constant<int, 3>{});
+    static_for<L / 2>([&](auto pc) __attribute__((always_inline)) { copy_pair(c, pc); });
   };
   if constexpr (CLAIMS) {
     if (tid == 0) {
@@ -586,7 +601,7 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, 2) gemm_fast_kernel(Par
     wait_vmcnt<L>();  // step 0's copy landed; step 1's may still fly
     __syncthreads();
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) read_b_frag(I0{}, sB0, 0, nb);
+    for (int nb = 0; nb < NB; ++nb) read_b_frag(I0{}, sB0, 0, nb);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) read_a_frag(I0{}, sA0, 0, mb);
   }
