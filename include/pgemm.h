@@ -66,7 +66,8 @@ typedef enum {
  *   w, then claims further tile ids from a device-wide atomic work counter
  *   until a claim fails, after which it never claims again -- the AMD
  *   analogue of cluster launch control's cancel-and-reuse (KernelWiki,
- *   intro), not a port of it.
+ *   intro), not a port of it. With G >= T there is nothing to claim and no
+ *   claim is made.
  * CANCEL: the grid is one workgroup per tile (T), as in NONPERSISTENT, but
  *   every workgroup claims its tiles -- the first one too -- from the work
  *   counter and keeps claiming until a claim fails. Workgroups that run

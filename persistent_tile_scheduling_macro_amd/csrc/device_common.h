@@ -124,7 +124,8 @@ __host__ __device__ inline void tile_coords(int t, const Params& p, int* pm, int
 //
 // Each workgroup makes exactly one failing claim, so a launch makes exactly
 // `total` claims (T for dynamic, T + G for cancel-and-reuse) and they return
-// the counter values 0..total-1 once each; the claim that returns total-1 is
+// the counter values 0..total-1 once each (a dynamic launch with G >= T, where
+// every workgroup has at most its own tile, makes no claim at all); the claim that returns total-1 is
 // the launch's last and resets the counter to 0 for the next launch on the
 // stream. A value outside [0, total) cannot come from this protocol and is
 // treated as a failed claim, so a corrupted counter never names a tile

@@ -579,7 +579,10 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, Tile<CFG>::MIN_WAVES_PE
         t0 = claim_tile(p.counter, T, claim_offset<SCHED>(G), claim_total<SCHED>(T, G));
         s_ring[0] = t0;
       }
-      const int t1 = t0 < T ? claim_tile(p.counter, T, claim_offset<SCHED>(G), claim_total<SCHED>(T, G)) : T;
+      // dynamic with G >= T: no tile lies beyond the grid's own, so no claim is made at all
+      // (the counter is left at 0); cancel-and-reuse always claims
+      const bool may_claim = SCHED == kCancel || G < T;
+      const int t1 = (t0 < T && may_claim) ? claim_tile(p.counter, T, claim_offset<SCHED>(G), claim_total<SCHED>(T, G)) : T;
       s_ring[1] = t1;
       claim_live = t1 < T;
     }

@@ -111,6 +111,8 @@ __global__ void __launch_bounds__(THREADS) gemm_generic_kernel(Params p) {
       break;
     } else if constexpr (SCHED == kStatic) {
       tile += p.G;
+    } else if (SCHED == kDynamic && p.G >= p.T) {
+      break; // no tile lies beyond the grid's own: no claim is made (the counter stays 0)
     } else {
       if (tid == 0) s_claim = claim_tile(p.counter, p.T, claim_offset<SCHED>(p.G), claim_total<SCHED>(p.T, p.G));
       __syncthreads();
