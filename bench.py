@@ -96,7 +96,8 @@ def source_digest() -> str:
 
 def measured_traffic(kernel: str, workload: str):
     """Calibrated HBM bytes per launch of `kernel` from the committed rocprofv3
-    summary, or None if there is none or the kernel source changed since."""
+    summary (one key line per kernel of the workload), or None if there is none
+    or the kernel source changed since."""
     try:
         kv = {}
         with open(TRAFFIC_FILE) as f:
@@ -106,10 +107,10 @@ def measured_traffic(kernel: str, workload: str):
                     kv[k.strip()] = v.strip()
     except OSError:
         return None
-    if kv.get("source_sha256") != source_digest() or kv.get("workload") != workload or kv.get("kernel") != kernel:
+    if kv.get("source_sha256") != source_digest() or kv.get("workload") != workload:
         return None
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return float(kv[f"hbm_bytes_per_launch {kernel}"])
     except (KeyError, ValueError):
         return None
 
