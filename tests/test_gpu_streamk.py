@@ -193,3 +193,29 @@ def test_generic_body_runs_streamk_as_static(pg):
         assert np.all(visits == 1)
     finally:
         pg.pgemm_destroy(h)
+
+
+def test_streamk_with_xcd_remap_and_a_deep_split(pg):
+    """Two corners of the split: (1) the XCD-aware tile remap on, where the
+    whole-wave launch covers only the first W*G tiles (the remap's chunk, the
+    CU count, divides W*G, so its tiles map exactly as in one launch); (2) a
+    single tile whose K is cut into a hundred or more pieces, all added by one
+    fix-up workgroup column. Small integers: bit-exact."""
+    dev = torch.device("cuda:0")
+    h = pg.pgemm_create(0)
+    try:
+        pg.pgemm_set_tile_config(h, pg.PGEMM_TILE_128)
+        pg.pgemm_set_tile_order(h, 4, True)
+        for (M, N, K, gm) in [(2176, 2176, 1024, 1), (128, 128, 65536, 0)]:
+            split = pg.pgemm_query_streamk(h, M, N, K, 0, gm)
+            say(f"case stream-K remap/deep {M}x{N}x{K} gm {gm}: {split}")
+            assert split["pieces_split"] > 0
+            A, B = si.operands(M, N, K, "f16", "small_int", workload=50)
+            want = oracle.round_to(oracle.gemm(si.bits(A), si.bits(B), "f16"), "f16")
+            C, info, visits, _ = run_sk(pg, h, A.to(dev), B.to(dev), M, N, K, "f16", gm)
+            assert np.array_equal(si.bits(C.cpu()), want)
+            assert np.all(visits == 1)
+        deep = pg.pgemm_query_streamk(h, 128, 128, 65536, 0, 0)
+        assert deep["split_tiles"] == 1 and deep["split_groups"] >= 100
+    finally:
+        pg.pgemm_destroy(h)
