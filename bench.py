@@ -83,14 +83,20 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_gemm_fast_f16_sweep4k
 
 
 def source_digest() -> str:
-    """sha256 over the kernel sources; HBM counters are only reported for the source they came from."""
+    """sha256 over the kernel sources' code (comments and blank space removed);
+    HBM counters are only reported for the code they came from."""
     import hashlib
+    import re
 
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
         if name.endswith((".h", ".hip")):
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+            with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+                text = f.read()
+            text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", " ", text)
+            text = " ".join(text.split())
+            h.update(name.encode() + b"\0" + text.encode())
     return h.hexdigest()
 
 

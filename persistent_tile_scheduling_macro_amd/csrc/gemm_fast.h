@@ -208,7 +208,7 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, Tile<CFG>::MIN_WAVES_PE
   __shared__ __attribute__((aligned(1024))) uint8_t sB0[B_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t sA1[A_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t sB1[B_BYTES];
-  __shared__ int s_ring[8]; // dynamic mode: tile id of tile-sequence number q at q % 8
+  __shared__ int s_ring[8]; // claiming modes: tile id of tile-sequence number q at q % 8
 
   auto bufA = [&](auto c) __attribute__((always_inline)) -> uint8_t* {
     return decltype(c)::value == 0 ? sA0 : sA1;
@@ -295,7 +295,8 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, Tile<CFG>::MIN_WAVES_PE
   // result written to s_ring after them, so the atomic's latency hides
   // behind the stores, and the next barrier publishes it before the copy
   // of that tile can begin. Keeping the claim code out of the k-loop keeps
-  // its registers out of the loop too.
+  // its registers out of the loop too. (Stream-K does not use tile_of: its
+  // work units come from the walkers below.)
   constexpr bool CLAIMS = SCHED == kDynamic || SCHED == kCancel;
   bool claim_live = false;    // thread 0 only: the last claim got a tile
   auto tile_of = [&](int q) __attribute__((always_inline)) -> int {
