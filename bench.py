@@ -67,6 +67,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample duration")
     ap.add_argument("--modes", default=None, help="comma-separated subset of scheduling modes (0..4)")
+    ap.add_argument("--no-small-k-latency", action="store_true",
+                    help="skip the 100-launch latency pass for K <= 512 (profiled runs: one launch per point)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured once as a HIP graph and replayed (launch overhead removed)")
     ap.add_argument("--hold-cus", type=int, default=64, help="uneven workload: CUs held by the co-running kernel")
@@ -237,6 +239,22 @@ def main():
             ev[s][i][1].record(stream)
     torch.cuda.synchronize()
 
+    # small-K latency: for K <= 512 the launch and fixed costs dominate, so each such
+    # (K, mode) point is also launched 100 times with an event pair around each launch
+    small_k = {}
+    for p in probs:
+        if p[2] > 512 or args.no_small_k_latency:
+            continue
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(100)]
+        for e0, e1 in evs:
+            e0.record(stream)
+            launch(p)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        us = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
+        small_k.setdefault(f"K={p[2]}", {})[MODE_NAMES[p[3]] + (f"@g{p[4]}" if p[4] else "")] = \
+            {"median_us": round(us[50], 2), "min_us": round(us[0], 2), "max_us": round(us[-1], 2)}
+
     graph_info = None
     if args.graph:
         # One step captured as a graph: the launches are capture-safe (no memsets; the claiming
@@ -345,6 +363,8 @@ def main():
         "timing": {"region_gpu_ms_per_step": round(region_ms / args.steps, 3),
                    "per_launch_pass_ms_per_step": round(sum(sum(v) for v in per.values()) / args.steps * 1e3, 3)},
     }
+    if small_k:
+        result["small_k_latency"] = small_k
     if graph_info:
         result["graph"] = graph_info
     if args.table:
@@ -488,8 +508,17 @@ def cpu_baseline(dtype, kind, wid, probs, seconds):
             flops += 2.0 * m * n * K
             done.append(f"{m}x{n}x{K}")
         sample = f"{len(done)} of the {len(todo)} problems of the workload in full ({', '.join(done)})"
+    # one thread on the smallest configured problem (256^3, the correctness configuration)
+    A1, B1 = si.operands(256, 256, 256, dtype, kind, workload=1)
+    a1, b1 = si.bits(A1), si.bits(B1)
+    t0 = time.perf_counter()
+    oracle.gemm(a1, b1, dtype, nthreads=1)
+    single = time.perf_counter() - t0
     return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{sample}, fp64 triple loop, {spent:.1f} s"}
+            "sample": f"{sample}, fp64 triple loop, {spent:.1f} s",
+            "seconds": round(spent, 2), "gflops_fp64": round(flops / spent / 1e9, 2),
+            "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "single_thread_256cubed_s": round(single, 4)}
 
 
 if __name__ == "__main__":
