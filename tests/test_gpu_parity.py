@@ -294,3 +294,31 @@ def test_graph_capture_and_replay(pg):
             assert pg.pgemm_read_work_counter(h) == 0
     finally:
         pg.pgemm_destroy(h)
+
+
+def test_size_limits_are_rejected_before_any_launch(pg):
+    """The fast kernel's buffer offsets are 32-bit: a tile's A rows (BM x K
+    elements) and a k-step's B rows (BK x N elements) must span < 2^31 bytes.
+    The planner refuses larger problems with PGEMM_ERR_UNSUPPORTED (checked
+    through the launch query, which plans exactly as pgemm_run does but
+    launches nothing), and accepts the largest ones inside the limits."""
+    h = pg.pgemm_create(0)
+    try:
+        pg.pgemm_set_tile_config(h, pg.PGEMM_TILE_256)
+        k_max = (1 << 31) // (256 * 2)  # 256 rows of fp16 A
+        ok = pg.pgemm_query_launch(h, 256, 256, k_max - 8, 0, 1, 0)
+        assert ok["fast_path"] == 1
+        for mode in (0, 1, 2, 3, 4):
+            with pytest.raises(pg.PgemmError) as e:
+                pg.pgemm_query_launch(h, 256, 256, k_max, 0, mode, 0)
+            assert e.value.status == pg.PGEMM_ERR_UNSUPPORTED, mode
+        n_max = (1 << 31) // (64 * 2)  # 64 k-rows of fp16 B
+        pg.pgemm_query_launch(h, 256, n_max - 8, 256, 0, 1, 0)
+        with pytest.raises(pg.PgemmError) as e:
+            pg.pgemm_query_launch(h, 256, n_max, 256, 0, 1, 0)
+        assert e.value.status == pg.PGEMM_ERR_UNSUPPORTED
+        with pytest.raises(pg.PgemmError) as e:  # sizes beyond int32
+            pg.pgemm_query_launch(h, 1 << 31, 256, 256, 0, 1, 0)
+        assert e.value.status == pg.PGEMM_ERR_UNSUPPORTED
+    finally:
+        pg.pgemm_destroy(h)
