@@ -35,6 +35,7 @@ struct pgemm_ctx {
   int sk_min_pairs = 4;
   float* work = nullptr; // stream-K partial tiles, grown on demand
   size_t work_bytes = 0;
+  int occ_cache[3][5][3] = {}; // occupancy per (dtype, mode, body); 0 = not queried yet
   char last_error[512] = {0};
 };
 
@@ -165,11 +166,16 @@ int plan_launch(pgemm_ctx* h, int64_t M, int64_t N, int64_t K, int dtype, int sc
     if ((int64_t)pl->bm * K * es >= ((int64_t)1 << 31) || (int64_t)pl->bk * N * es >= ((int64_t)1 << 31))
       return fail(h, PGEMM_ERR_UNSUPPORTED, "operand rows too long for 32-bit buffer offsets");
   }
-  kernel_fn k = pick_kernel(dtype, sched, pl->body);
-  int occ = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(k), pl->threads, 0);
-  if (e != hipSuccess) return fail(h, PGEMM_ERR_HIP, "occupancy query: %s", hipGetErrorString(e));
-  if (occ < 1) occ = 1;
+  // occupancy of the kernel, queried once per handle (it depends on the kernel and the device only)
+  int& cached = h->occ_cache[dtype][sched][pl->body];
+  if (cached == 0) {
+    kernel_fn k = pick_kernel(dtype, sched, pl->body);
+    int q = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&q, reinterpret_cast<const void*>(k), pl->threads, 0);
+    if (e != hipSuccess) return fail(h, PGEMM_ERR_HIP, "occupancy query: %s", hipGetErrorString(e));
+    cached = q < 1 ? 1 : q;
+  }
+  const int occ = cached;
   pl->occupancy = occ;
   const int64_t mult = grid_multiple <= 0 ? occ : grid_multiple;
   if (sched == kNonPersistent || sched == kCancel) {
