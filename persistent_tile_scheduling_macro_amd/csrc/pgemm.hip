@@ -230,7 +230,7 @@ int pgemm_create(pgemm_handle_t* out, int device) {
     return PGEMM_ERR_OOM;
   }
   if (hipMemset(h->counter, 0, 256) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
-    hipFree(h->counter);
+    (void)hipFree(h->counter);
     delete h;
     return PGEMM_ERR_HIP;
   }
@@ -299,7 +299,7 @@ int pgemm_run(pgemm_handle_t h, const void* A, const void* B, void* C, int64_t M
     if (pl.work_bytes > h->work_bytes) {
       // grow the workspace: wait for launches that may still use the old one
       if (hipStreamSynchronize(h->stream) != hipSuccess) return fail(h, PGEMM_ERR_HIP, "stream synchronize failed");
-      if (h->work) hipFree(h->work);
+      if (h->work) (void)hipFree(h->work);
       h->work = nullptr;
       h->work_bytes = 0;
       if (hipMalloc(&h->work, pl.work_bytes) != hipSuccess) {
