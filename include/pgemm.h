@@ -210,9 +210,11 @@ int pgemm_query_streamk(pgemm_handle_t h, int64_t M, int64_t N, int64_t K, int d
 
 /* Tile-order knobs: GROUP_SIZE_M of the grouped order (default 4; the
  * Triton issue's setting is 8; 1 = row-major), and the XCD-aware remap
- * (1 = on; 0 = off, the default). Both apply identically to all modes. The
- * environment variables PGEMM_GROUP_M and PGEMM_XCD_REMAP override the
- * defaults at pgemm_create. */
+ * (1 = on; 0 = off; -1 = automatic, the default: on for launches with more
+ * tiles than the device has CUs, off otherwise). Both apply identically to
+ * all modes and never change C's bits, only which workgroup computes which
+ * tile. The environment variables PGEMM_GROUP_M and PGEMM_XCD_REMAP override
+ * the defaults at pgemm_create. */
 int pgemm_set_tile_order(pgemm_handle_t h, int group_m, int xcd_remap);
 
 /* Choose the fast kernel's macro tile for later runs on this handle

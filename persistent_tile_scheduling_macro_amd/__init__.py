@@ -163,8 +163,13 @@ def pgemm_query_streamk(h, M: int, N: int, K: int, dtype: int, grid_multiple: in
     return d
 
 
-def pgemm_set_tile_order(h, group_m: int = 8, xcd_remap: bool = True) -> None:
-    _check(_set_tile_order(h, int(group_m), int(bool(xcd_remap))), h)
+def pgemm_set_tile_order(h, group_m: int = 8, xcd_remap=True) -> None:
+    """xcd_remap: True/1 on, False/0 off, None/-1 automatic (on when a launch has more tiles than CUs)."""
+    if xcd_remap is None or (not isinstance(xcd_remap, bool) and int(xcd_remap) < 0):
+        v = -1
+    else:
+        v = int(bool(xcd_remap))
+    _check(_set_tile_order(h, int(group_m), v), h)
 
 
 def pgemm_set_tile_config(h, tile: int) -> None:

@@ -25,10 +25,14 @@ struct pgemm_ctx {
   int32_t* owner = nullptr;
   int64_t n_owner = 0;
   // Tile-order defaults measured on MI355X (8192^3 and 4096^3 fp16, round-robin
-  // timing): the XCD remap did not help and GROUP_SIZE_M between 1 and 16 moved
-  // throughput by a few percent at most.
+  // timing): GROUP_SIZE_M between 1 and 16 moved throughput by a few percent
+  // at most. The XCD remap (-1 = automatic: on when a launch has more tiles
+  // than CUs) leaves the time level at 8192^3 and cuts the L2-miss fetches
+  // there by a third (each XCD reads fewer operand panels); with one wave of
+  // tiles it fetches the same bytes and measured slightly slower, so it stays
+  // off there.
   int group_m = 4;
-  int xcd_remap = 0;
+  int xcd_remap = -1;
   int tile = PGEMM_TILE_AUTO; // macro-tile choice of the fast kernel
   // Stream-K: shortest piece, in k-step pairs, a split may cut (tiles with
   // fewer pairs are not split).
@@ -235,7 +239,7 @@ int pgemm_create(pgemm_handle_t* out, int device) {
     return PGEMM_ERR_HIP;
   }
   if (const char* g = getenv("PGEMM_GROUP_M")) h->group_m = std::max(1, atoi(g));
-  if (const char* x = getenv("PGEMM_XCD_REMAP")) h->xcd_remap = atoi(x) != 0;
+  if (const char* x = getenv("PGEMM_XCD_REMAP")) h->xcd_remap = atoi(x) < 0 ? -1 : atoi(x) != 0;
   if (const char* m = getenv("PGEMM_SK_MIN_PAIRS")) h->sk_min_pairs = std::max(1, atoi(m));
   if (const char* t = getenv("PGEMM_TILE")) {
     const int v = atoi(t);
@@ -287,7 +291,7 @@ int pgemm_run(pgemm_handle_t h, const void* A, const void* B, void* C, int64_t M
   p.T = (int)pl.T;
   p.G = (int)pl.G;
   p.group_m = h->group_m;
-  p.xcd_chunk = h->xcd_remap ? h->cus : 0;
+  p.xcd_chunk = (h->xcd_remap > 0 || (h->xcd_remap < 0 && pl.T > h->cus)) ? h->cus : 0;
   p.counter = h->counter;
   p.visits = h->visits;
   p.owner = h->owner;
@@ -434,7 +438,7 @@ int pgemm_set_tile_order(pgemm_handle_t h, int group_m, int xcd_remap) {
   if (!h) return PGEMM_ERR_INVALID_ARG;
   if (group_m < 1) return fail(h, PGEMM_ERR_INVALID_ARG, "group_m must be >= 1");
   h->group_m = group_m;
-  h->xcd_remap = xcd_remap != 0;
+  h->xcd_remap = xcd_remap < 0 ? -1 : xcd_remap != 0;
   return PGEMM_OK;
 }
 

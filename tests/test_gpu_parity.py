@@ -196,6 +196,28 @@ def test_static_owner_map_and_dynamic_counter(pg, handle):
     assert np.array_equal(si.bits(C.cpu()), want)
 
 
+def test_xcd_remap_settings_give_the_same_bits(pg, handle):
+    """The XCD remap (off, on, automatic) only moves tiles between
+    workgroups: on a problem with more tiles than CUs (so the automatic
+    setting turns it on) C is bit-exact against the oracle and every tile is
+    written once, in every tile-scheduling mode."""
+    M, N, K = 4352, 4352, 64  # 289 tiles of 256 x 256, 1156 of 128 x 128
+    A, B = si.operands(M, N, K, "f16", "small_int", workload=3)
+    want = oracle.round_to(oracle.gemm(si.bits(A), si.bits(B), "f16"), "f16")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    try:
+        for remap in (0, 1, None):
+            pg.pgemm_set_tile_order(handle, 4, remap)
+            for mode in SAME_BITS:
+                say(f"case xcd remap {remap} mode {mode} {M}x{N}x{K}")
+                c, v, info = run(pg, handle, A, B, "f16", mode)
+                assert info["tiles"] > cus
+                assert np.array_equal(c, want), (remap, mode)
+                assert (v == 1).all(), (remap, mode)
+    finally:
+        pg.pgemm_set_tile_order(handle, 4, None)
+
+
 def test_degenerate_sizes(pg, handle):
     dev = torch.device("cuda:0")
     A = torch.ones((5, 0), dtype=torch.float16, device=dev)
