@@ -405,6 +405,8 @@ int pgemm_query_launch(pgemm_handle_t h, int64_t M, int64_t N, int64_t K, int dt
                        int* fast_path) {
   int rc = check_common(h, M, N, K, dtype, sched_mode);
   if (rc != PGEMM_OK) return rc;
+  // the plan may query the kernel's occupancy: on the handle's device
+  if (hipSetDevice(h->device) != hipSuccess) return fail(h, PGEMM_ERR_HIP, "hipSetDevice failed");
   Plan pl;
   rc = plan_launch(h, M, N, K, dtype, sched_mode, grid_multiple, sizes_fast(dtype, N, K), &pl);
   if (rc != PGEMM_OK) return rc;
@@ -423,6 +425,7 @@ int pgemm_query_streamk(pgemm_handle_t h, int64_t M, int64_t N, int64_t K, int d
                         int64_t* workspace_bytes) {
   int rc = check_common(h, M, N, K, dtype, PGEMM_SCHED_STREAMK);
   if (rc != PGEMM_OK) return rc;
+  if (hipSetDevice(h->device) != hipSuccess) return fail(h, PGEMM_ERR_HIP, "hipSetDevice failed");
   Plan pl;
   rc = plan_launch(h, M, N, K, dtype, PGEMM_SCHED_STREAMK, grid_multiple, sizes_fast(dtype, N, K), &pl);
   if (rc != PGEMM_OK) return rc;
