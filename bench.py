@@ -73,6 +73,9 @@ def parse():
                     help="also time the step captured once as a HIP graph and replayed (launch overhead removed)")
     ap.add_argument("--hold-cus", type=int, default=64, help="uneven workload: CUs held by the co-running kernel")
     ap.add_argument("--hold-us", type=int, default=6000, help="uneven workload: how long they are held")
+    ap.add_argument("--trace", action="store_true",
+                    help="after timing, run every (problem, mode) once more with the tile trace on (untimed) and "
+                         "report makespan, busy fraction of the workgroup slots and the drain (tail) time")
     ap.add_argument("--tile", default="auto", choices=["auto", "256", "128"],
                     help="macro tile of the fast kernel (auto: the library's default choice)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -341,6 +344,10 @@ def main():
         ps = [p for p in probs if p[3] == mode]
         mode_tflops[MODE_NAMES[mode]] = round(sum(flops[p] for p in ps) / sum(float(np.median(per[p])) for p in ps) / 1e12, 1)
 
+    trace_info = None
+    if args.trace:
+        trace_info = tile_trace_summary(pg, h, probs, operands, outs, dt_code, torch, np)
+
     pg.pgemm_destroy(h)
 
     cpu = None
@@ -367,10 +374,72 @@ def main():
         result["small_k_latency"] = small_k
     if graph_info:
         result["graph"] = graph_info
+    if trace_info:
+        result["tile_trace"] = trace_info
     if args.table:
         with open(args.table, "w") as f:
             json.dump({"result": result, "table": table}, f, indent=1)
     print(json.dumps(result), flush=True)
+
+
+def drain_start(st, en, slots, np):
+    """Time at which the chip stops being full for good: the tiles in flight
+    (+1 at each start, -1 at each end, ends first on equal times) last equal
+    `slots` before the next event, which is where the drain begins. Returns
+    the first start when the slots were never all busy."""
+    n = len(st)
+    ev = np.concatenate([np.stack([st, np.ones(n, np.int64)], 1), np.stack([en, -np.ones(n, np.int64)], 1)])
+    ev = ev[np.lexsort((ev[:, 1], ev[:, 0]))]
+    level = np.cumsum(ev[:, 1])
+    full = np.flatnonzero(level >= slots)
+    if not len(full):
+        return int(st.min())
+    nxt = full[-1] + 1
+    return int(ev[nxt, 0]) if nxt < len(ev) else int(en.max())
+
+
+def tile_trace_summary(pg, h, probs, operands, outs, dt_code, torch, np):
+    """One untimed run per (problem, mode) with the tile trace on. Per run:
+    makespan (first tile start to last tile end), the busy fraction of the
+    workgroup slots (CUs x occupancy) over the makespan, and the drain: the
+    time from the last moment every slot held a tile to the end -- the tail
+    that the last, partial wave of tiles leaves (KernelWiki "Persistent
+    Kernels with Cluster Launch Control", "Choosing between static and CLC
+    scheduling"). Stream-K tail pieces are not traced (the fix-up stores
+    their tiles), so its busy fraction counts only whole tiles and fix-ups."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    khz = pg.pgemm_clock_khz(0)
+    out = {}
+    for p in probs:
+        m, n, K, mode, gm = p
+        info = pg.pgemm_query_launch(h, m, n, K, dt_code, mode, gm)
+        T = info["tiles"]
+        slots = cus * info["occupancy"]
+        tr = torch.zeros(4 * T, dtype=torch.int64, device="cuda:0")
+        A, B = operands[(m, n, K)]
+        pg.pgemm_set_tile_trace(h, tr)
+        try:
+            pg.pgemm_run(h, A, B, outs[(m, n)], m, n, K, dt_code, mode, gm)
+            torch.cuda.synchronize()
+        finally:
+            pg.pgemm_set_tile_trace(h, None)
+        t = tr.view(T, 4).cpu().numpy()
+        wg, xcd, st, en = t[:, 0], t[:, 1], t[:, 2], t[:, 3]
+        t0, t1 = int(st.min()), int(en.max())
+        us = 1e3 / khz  # microseconds per tick
+        busy = float((en - st).sum())
+        drain_from = drain_start(st, en, slots, np)
+        own = wg >= 0
+        key = f"{m}x{n}x{K}"
+        out.setdefault(key, {})[MODE_NAMES[mode] + (f"@g{gm}" if gm else "")] = {
+            "tiles": T, "grid": info["grid"], "slots": slots,
+            "makespan_us": round((t1 - t0) * us, 1),
+            "busy_frac": round(busy / (slots * (t1 - t0)), 4) if t1 > t0 else None,
+            "drain_us": round((t1 - drain_from) * us, 1),
+            "tile_us_median": round(float(np.median(en - st)) * us, 1),
+            "xcd_is_wg_mod_8": round(float((xcd[own] == wg[own] % 8).mean()), 4) if own.any() else None,
+        }
+    return out
 
 
 def run_uneven(args, pg, si, torch, np):

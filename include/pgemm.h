@@ -188,6 +188,29 @@ int pgemm_set_tile_counter(pgemm_handle_t h, int32_t* dev_visits, int64_t n_tile
  * every tile still reads 1. */
 int pgemm_set_owner_log(pgemm_handle_t h, int32_t* dev_owner, int64_t n_tiles);
 
+/* Attach a caller-owned device int64 array of 4 * n_tiles entries: the
+ * tile trace, used to draw per-workgroup timelines of the tail effect
+ * (KernelWiki "Persistent Kernels with Cluster Launch Control", "Choosing
+ * between static and CLC scheduling": the last wave of tiles leaves part
+ * of the chip idle). Each run writes, for every tile t,
+ *   trace[4t+0]  id of the workgroup that stored tile t (the owner-log
+ *                convention: -1 - s for a STREAMK split tile, which the
+ *                fix-up launch stores),
+ *   trace[4t+1]  id of the XCD (0..7) whose CU ran that workgroup,
+ *   trace[4t+2]  start: when that workgroup began the tile (its k-loop),
+ *   trace[4t+3]  end: after the tile's C store was issued,
+ * the times in ticks of the device's constant-rate clock (see
+ * pgemm_clock_khz). For a split tile, start and end bracket its fix-up.
+ * The trace adds a clock read and a few stores per tile: leave it off in
+ * timed runs. NULL detaches. Runs whose tile count exceeds n_tiles fail
+ * with PGEMM_ERR_INVALID_ARG before launching. */
+int pgemm_set_tile_trace(pgemm_handle_t h, int64_t* dev_trace, int64_t n_tiles);
+
+/* Rate in kHz of the constant-rate clock that stamps the tile trace, for
+ * device `device`. PGEMM_ERR_INVALID_ARG if khz is NULL, PGEMM_ERR_HIP if
+ * the device cannot be queried. */
+int pgemm_clock_khz(int device, int* khz);
+
 /* Report how pgemm_run would launch this problem, without launching:
  * tile count, grid size, occupancy (workgroups per CU), macro tile
  * (bm x bn, k-step bk in elements), and whether the fast kernel is used.

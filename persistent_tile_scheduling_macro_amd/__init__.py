@@ -62,6 +62,8 @@ _status_string = _sig("pgemm_status_string", ctypes.c_char_p, _int)
 _last_error = _sig("pgemm_last_error", ctypes.c_char_p, _vp)
 _set_tile_counter = _sig("pgemm_set_tile_counter", _int, _vp, _vp, _i64)
 _set_owner_log = _sig("pgemm_set_owner_log", _int, _vp, _vp, _i64)
+_set_tile_trace = _sig("pgemm_set_tile_trace", _int, _vp, _vp, _i64)
+_clock_khz = _sig("pgemm_clock_khz", _int, _int, _ip)
 _query_launch = _sig("pgemm_query_launch", _int, _vp, _i64, _i64, _i64, _int, _int, _int,
                      _ip, _ip, _ip, _ip, _ip, _ip, _ip)
 _query_streamk = _sig("pgemm_query_streamk", _int, _vp, _i64, _i64, _i64, _int, _int, _ip, _ip, _ip, _ip,
@@ -142,6 +144,19 @@ def pgemm_set_owner_log(h, owner, n_tiles: int = 0) -> None:
     if owner is not None and not isinstance(owner, int) and not n_tiles:
         n_tiles = owner.numel()
     _check(_set_owner_log(h, _ptr(owner) or None, int(n_tiles)), h)
+
+
+def pgemm_set_tile_trace(h, trace, n_tiles: int = 0) -> None:
+    """trace: int64 device tensor of 4 * n_tiles entries ({wg, xcd, start, end} per tile), or None."""
+    if trace is not None and not isinstance(trace, int) and not n_tiles:
+        n_tiles = trace.numel() // 4
+    _check(_set_tile_trace(h, _ptr(trace) or None, int(n_tiles)), h)
+
+
+def pgemm_clock_khz(device: int = 0) -> int:
+    v = ctypes.c_int()
+    _check(_clock_khz(int(device), ctypes.byref(v)))
+    return v.value
 
 
 def pgemm_query_launch(h, M: int, N: int, K: int, dtype: int, sched_mode: int, grid_multiple: int = 0) -> dict:

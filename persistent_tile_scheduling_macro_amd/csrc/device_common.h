@@ -66,6 +66,7 @@ struct Params {
   int* counter;    // dynamic scheduler's work counter (reads 0 between launches)
   int* visits;     // optional int32[T] tile-visit counter
   int* owner;      // optional int32[T] owner log (workgroup id per tile)
+  long long* trace; // optional int64[4T] tile trace {workgroup, XCD, start, end}
   // stream-K only (zero otherwise): the first T - sk_tiles tiles run whole,
   // sk_waves per workgroup; the k-step pairs of the last sk_tiles tiles are
   // split over workgroups 0 .. sk_groups-1; pieces that do not cover their
@@ -244,6 +245,26 @@ struct SkWalker {
     return true;
   }
 };
+
+// ------------------------------------------------------- tile trace
+// Optional per-tile record of who ran a tile, where and when: entry t holds
+// {workgroup id, XCD id, start, end}, the times in ticks of the device's
+// constant-rate clock. Kernels consume each clock read at once (an empty
+// asm use or a store), so no scalar memory read stays outstanding across
+// a k-loop.
+__device__ inline long long trace_clock() { return (long long)__builtin_amdgcn_s_memrealtime(); }
+__device__ inline int xcd_id() {
+  int v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+  return v & 15;
+}
+__device__ inline void trace_tile(long long* trace, int t, int wg, long long start, long long end) {
+  long long* e = trace + 4 * (long long)t;
+  e[0] = wg;
+  e[1] = xcd_id();
+  e[2] = start;
+  e[3] = end;
+}
 
 // ------------------------------------------------ buffer loads into LDS
 // gfx9 buffer resource word 3 for raw (untyped) dword access.

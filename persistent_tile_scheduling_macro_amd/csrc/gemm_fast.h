@@ -174,7 +174,10 @@ __device__ inline typename Frag<DT>::t read_a(const uint8_t* lo, const uint8_t* 
   }
 }
 
-template <int DT, int SCHED, int CFG>
+// TRACE selects the instantiation that writes the tile trace (p.trace); the
+// timed kernels carry no trace code at all, so their register allocation is
+// untouched by it.
+template <int DT, int SCHED, int CFG, bool TRACE>
 __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, Tile<CFG>::MIN_WAVES_PER_SIMD) gemm_fast_kernel(Params p) {
   constexpr int BM = Tile<CFG>::BM, BN = Tile<CFG>::BN;
   constexpr int WAVES = Tile<CFG>::WAVES, THREADS = WAVES * 64;
@@ -421,6 +424,10 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, Tile<CFG>::MIN_WAVES_PE
     for (int nb = 0; nb < NB; ++nb) mfma_acc(acc[mb][nb], bf[F][nb], af[F][mb]);
   };
 
+  // tile trace: when the current unit began (each clock value is consumed at
+  // once, so no scalar read is outstanding in the k-loop)
+  long long t_begin = 0;
+
   // ---- epilogue: round to the output type and store one tile ---------------
   auto epilogue = [&](int tile) __attribute__((always_inline)) {
     acc_drain();
@@ -483,6 +490,11 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, Tile<CFG>::MIN_WAVES_PE
       if (p.visits) atomicAdd(p.visits + tile, 1);
       if (p.owner) p.owner[tile] = blockIdx.x;
     }
+    if constexpr (TRACE) {
+      const long long te = trace_clock();
+      if (tid == 0) trace_tile(p.trace, tile, blockIdx.x, t_begin, te);
+      t_begin = te;
+    }
   };
 
   // ---- stream-K: store the fp32 partial tile of a piece ---------------------
@@ -502,6 +514,10 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, Tile<CFG>::MIN_WAVES_PE
         *reinterpret_cast<floatx4_t*>(row + col) = acc_read(acc[mb][nb]);
       }
       __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (TRACE) {
+      t_begin = trace_clock();
+      asm volatile("" ::"s"(t_begin));
     }
   };
 
@@ -611,6 +627,10 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, Tile<CFG>::MIN_WAVES_PE
   }
   int c_q = 0; // consumer tile sequence number
   if constexpr (!SK) c_tile = tile_of(0);
+  if constexpr (TRACE) {
+    t_begin = trace_clock();
+    asm volatile("" ::"s"(t_begin));
+  }
   for (;;) {
     zero_acc();
     for (int kt = c_kb; kt < c_ke; kt += 2) {
@@ -662,6 +682,11 @@ __global__ void __launch_bounds__(256) sk_fixup_kernel(Params p) {
   const int w1 = sk_owner((int64_t)(s + 1) * kp - 1, S, p.sk_groups);
   if (w0 == w1) return;
   const int tile = p.T - p.sk_tiles + s;
+  long long t_begin = 0;
+  if (p.trace) {
+    t_begin = trace_clock();
+    asm volatile("" ::"s"(t_begin));
+  }
   int pm, pn;
   tile_coords(tile, p, &pm, &pn);
   const int r = blockIdx.y * ROWS + (int)threadIdx.x / TPR;
@@ -681,6 +706,7 @@ __global__ void __launch_bounds__(256) sk_fixup_kernel(Params p) {
   if (blockIdx.y == 0 && threadIdx.x == 0) {
     if (p.visits) atomicAdd(p.visits + tile, 1);
     if (p.owner) p.owner[tile] = -1 - s; // stored by the fix-up, not by a workgroup of the GEMM grid
+    if (p.trace) trace_tile(p.trace, tile, -1 - s, t_begin, trace_clock());
   }
 }
 

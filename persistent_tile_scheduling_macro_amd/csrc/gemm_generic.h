@@ -47,6 +47,11 @@ __global__ void __launch_bounds__(THREADS) gemm_generic_kernel(Params p) {
     __syncthreads();
   }
   while (tile < p.T) {
+    long long t_begin = 0;
+    if (p.trace) {
+      t_begin = trace_clock();
+      asm volatile("" ::"s"(t_begin));
+    }
     int pm, pn;
     tile_coords(tile, p, &pm, &pn);
     const int m0 = pm * BM, n0 = pn * BN;
@@ -106,6 +111,7 @@ __global__ void __launch_bounds__(THREADS) gemm_generic_kernel(Params p) {
     if (tid == 0) {
       if (p.visits) atomicAdd(p.visits + tile, 1);
       if (p.owner) p.owner[tile] = blockIdx.x;
+      if (p.trace) trace_tile(p.trace, tile, blockIdx.x, t_begin, trace_clock());
     }
     if constexpr (SCHED == kNonPersistent) {
       break;

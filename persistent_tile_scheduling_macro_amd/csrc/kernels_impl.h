@@ -9,23 +9,27 @@
 namespace pgemm {
 
 template <int DT, int SCHED>
-kernel_fn pick_body(int body) {
+kernel_fn pick_body(int body, bool trace) {
   switch (body) {
-    case kBodyTile256: return fast::gemm_fast_kernel<DT, SCHED, fast::kTile256>;
-    case kBodyTile128: return fast::gemm_fast_kernel<DT, SCHED, fast::kTile128>;
+    case kBodyTile256:
+      return trace ? fast::gemm_fast_kernel<DT, SCHED, fast::kTile256, true>
+                   : fast::gemm_fast_kernel<DT, SCHED, fast::kTile256, false>;
+    case kBodyTile128:
+      return trace ? fast::gemm_fast_kernel<DT, SCHED, fast::kTile128, true>
+                   : fast::gemm_fast_kernel<DT, SCHED, fast::kTile128, false>;
     default: // the generic body has no stream-K split: it runs that mode as static
       return generic::gemm_generic_kernel<DT, SCHED == kStreamK ? kStatic : SCHED>;
   }
 }
 
 template <int DT>
-kernel_fn pick_for_dtype(int sched, int body) {
+kernel_fn pick_for_dtype(int sched, int body, bool trace) {
   switch (sched) {
-    case kNonPersistent: return pick_body<DT, kNonPersistent>(body);
-    case kStatic: return pick_body<DT, kStatic>(body);
-    case kDynamic: return pick_body<DT, kDynamic>(body);
-    case kCancel: return pick_body<DT, kCancel>(body);
-    default: return pick_body<DT, kStreamK>(body);
+    case kNonPersistent: return pick_body<DT, kNonPersistent>(body, trace);
+    case kStatic: return pick_body<DT, kStatic>(body, trace);
+    case kDynamic: return pick_body<DT, kDynamic>(body, trace);
+    case kCancel: return pick_body<DT, kCancel>(body, trace);
+    default: return pick_body<DT, kStreamK>(body, trace);
   }
 }
 

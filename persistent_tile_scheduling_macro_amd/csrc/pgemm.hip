@@ -24,6 +24,8 @@ struct pgemm_ctx {
   int64_t n_visits = 0;
   int32_t* owner = nullptr;
   int64_t n_owner = 0;
+  int64_t* trace = nullptr;
+  int64_t n_trace = 0;
   // Tile-order defaults measured on MI355X (8192^3 and 4096^3 fp16, round-robin
   // timing): GROUP_SIZE_M between 1 and 16 moved throughput by a few percent
   // at most. The XCD remap (-1 = automatic: on when a launch has more tiles
@@ -69,11 +71,11 @@ BodyShape body_shape(int body) {
 }
 int fast_block_k(int dtype) { return dtype == kF8E4M3 ? 128 : 64; }
 
-kernel_fn pick_kernel(int dtype, int sched, int body) {
+kernel_fn pick_kernel(int dtype, int sched, int body, bool trace = false) {
   switch (dtype) {
-    case kF16: return pick_kernel_f16(sched, body);
-    case kBF16: return pick_kernel_bf16(sched, body);
-    default: return pick_kernel_f8(sched, body);
+    case kF16: return pick_kernel_f16(sched, body, trace);
+    case kBF16: return pick_kernel_bf16(sched, body, trace);
+    default: return pick_kernel_f8(sched, body, trace);
   }
 }
 
@@ -279,6 +281,9 @@ int pgemm_run(pgemm_handle_t h, const void* A, const void* B, void* C, int64_t M
   if (h->owner && pl.T > h->n_owner)
     return fail(h, PGEMM_ERR_INVALID_ARG, "owner log holds %lld entries, run has %lld tiles", (long long)h->n_owner,
                 (long long)pl.T);
+  if (h->trace && pl.T > h->n_trace)
+    return fail(h, PGEMM_ERR_INVALID_ARG, "tile trace holds %lld tiles, run has %lld tiles", (long long)h->n_trace,
+                (long long)pl.T);
   Params p;
   p.A = static_cast<const uint8_t*>(A);
   p.B = static_cast<const uint8_t*>(B);
@@ -295,6 +300,7 @@ int pgemm_run(pgemm_handle_t h, const void* A, const void* B, void* C, int64_t M
   p.counter = h->counter;
   p.visits = h->visits;
   p.owner = h->owner;
+  p.trace = reinterpret_cast<long long*>(h->trace);
   p.sk_waves = pl.sk_waves;
   p.sk_tiles = pl.sk_tiles;
   p.sk_groups = pl.sk_groups;
@@ -316,7 +322,7 @@ int pgemm_run(pgemm_handle_t h, const void* A, const void* B, void* C, int64_t M
     p.work = h->work;
   }
   if (sched_mode != kStreamK || !pl.fast) {
-    kernel_fn k = pick_kernel(dtype, sched_mode, pl.body);
+    kernel_fn k = pick_kernel(dtype, sched_mode, pl.body, p.trace != nullptr);
     hipLaunchKernelGGL(k, dim3((unsigned)pl.G), dim3(pl.threads), 0, h->stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(h, PGEMM_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
@@ -336,7 +342,8 @@ int pgemm_run(pgemm_handle_t h, const void* A, const void* B, void* C, int64_t M
     pd.T = (int)(pl.T - pl.sk_tiles); // W * G
     pd.sk_waves = pd.sk_tiles = pd.sk_groups = 0;
     pd.work = nullptr;
-    hipLaunchKernelGGL(pick_kernel(dtype, kStatic, pl.body), dim3((unsigned)pl.G), dim3(pl.threads), 0, h->stream, pd);
+    hipLaunchKernelGGL(pick_kernel(dtype, kStatic, pl.body, p.trace != nullptr), dim3((unsigned)pl.G), dim3(pl.threads), 0,
+                       h->stream, pd);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(h, PGEMM_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
   }
@@ -344,8 +351,8 @@ int pgemm_run(pgemm_handle_t h, const void* A, const void* B, void* C, int64_t M
     Params ps = p;
     ps.sk_waves = 0;
     ps.G = pl.sk_groups;
-    hipLaunchKernelGGL(pick_kernel(dtype, kStreamK, pl.body), dim3((unsigned)pl.sk_groups), dim3(pl.threads), 0,
-                       h->stream, ps);
+    hipLaunchKernelGGL(pick_kernel(dtype, kStreamK, pl.body, p.trace != nullptr), dim3((unsigned)pl.sk_groups),
+                       dim3(pl.threads), 0, h->stream, ps);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(h, PGEMM_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
     if (pl.sk_split) {
@@ -397,6 +404,23 @@ int pgemm_set_owner_log(pgemm_handle_t h, int32_t* dev_owner, int64_t n_tiles) {
   if (dev_owner && n_tiles <= 0) return fail(h, PGEMM_ERR_INVALID_ARG, "n_tiles must be positive");
   h->owner = dev_owner;
   h->n_owner = dev_owner ? n_tiles : 0;
+  return PGEMM_OK;
+}
+
+int pgemm_set_tile_trace(pgemm_handle_t h, int64_t* dev_trace, int64_t n_tiles) {
+  if (!h) return PGEMM_ERR_INVALID_ARG;
+  if (dev_trace && n_tiles <= 0) return fail(h, PGEMM_ERR_INVALID_ARG, "n_tiles must be positive");
+  h->trace = dev_trace;
+  h->n_trace = dev_trace ? n_tiles : 0;
+  return PGEMM_OK;
+}
+
+int pgemm_clock_khz(int device, int* khz) {
+  if (!khz) return PGEMM_ERR_INVALID_ARG;
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeWallClockRate, device) != hipSuccess || v <= 0)
+    return PGEMM_ERR_HIP;
+  *khz = v;
   return PGEMM_OK;
 }
 

@@ -121,3 +121,13 @@ def test_streamk_mode_constant_matches_the_header(pg):
     m = re.search(r"PGEMM_SCHED_STREAMK\s*=\s*(\d+)", text)
     assert m and int(m.group(1)) == pg.PGEMM_SCHED_STREAMK == 4
     assert pg.SCHED_NAMES["streamk"] == 4
+
+
+def test_tile_trace_argument_checks(pg):
+    """The trace entry points reject a null handle or output pointer without a device."""
+    with pytest.raises(pg.PgemmError) as e:
+        pg.pgemm_set_tile_trace(None, None)
+    assert e.value.status == pg.PGEMM_ERR_INVALID_ARG
+    lib = ctypes.CDLL(pg.LIB_PATH)
+    lib.pgemm_clock_khz.argtypes = [ctypes.c_int, ctypes.c_void_p]
+    assert lib.pgemm_clock_khz(0, None) == pg.PGEMM_ERR_INVALID_ARG

@@ -1,0 +1,26 @@
+"""CPU check of the benchmark's tail measure on hand-made tile traces."""
+import numpy as np
+
+import bench
+
+
+def test_drain_starts_when_the_first_slot_runs_dry():
+    # 4 slots: workgroup 0 runs three back-to-back tiles of 10, the others two; starts staggered
+    st, en = [], []
+    for w in range(4):
+        t = w
+        for _ in range(3 if w == 0 else 2):
+            st.append(t)
+            en.append(t + 10)
+            t += 10
+    st, en = np.array(st), np.array(en)
+    # full from t=3; workgroup 1 ends its last tile at 21 and nothing replaces it
+    assert bench.drain_start(st, en, 4, np) == 21
+
+
+def test_drain_with_no_events_inside_a_wave():
+    # two aligned waves of 3 slots and a third partial one: full until the second wave ends
+    st = np.array([0, 0, 0, 100, 100, 100, 200])
+    en = np.array([100, 100, 100, 200, 200, 200, 300])
+    assert bench.drain_start(st, en, 3, np) == 200
+    assert bench.drain_start(st, en, 4, np) == 0  # never full: the drain is the whole run
