@@ -57,12 +57,37 @@ WORKLOADS = {
 }
 
 
+def add_custom_workload(args) -> None:
+    """Register the 'custom' workload from the command line (same shape as the configured ones)."""
+    lo, hi = args.K_range
+    if min(args.M, args.N, lo, args.K_step) < 1 or hi < lo:
+        raise SystemExit("custom workload: --M, --N, --K-range and --K-step must be positive, with LO <= HI")
+    dtype = {"fp16": "f16", "bf16": "bf16", "fp8": "e4m3fn"}[args.prec]
+    modes = [int(x) for x in args.modes.split(",")] if args.modes else [0, 1, 2]
+    gms = [int(x) for x in args.grid_multiples.split(",")]
+    desc = (f"{args.prec} GEMM M={args.M} N={args.N}, K={lo}..{hi} step {args.K_step}, {args.input} inputs, "
+            f"fp32 accumulate; modes {modes}, grid multiples {gms}")
+    WORKLOADS["custom"] = (desc, dtype, args.M, args.N, list(range(lo, hi + 1, args.K_step)), modes, gms,
+                           args.input, 20)
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="sweep4k", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="sweep4k", choices=sorted(WORKLOADS) + ["custom"],
+                    help="a configured workload, or 'custom' built from --prec/--M/--N/--K-range/--K-step")
+    ap.add_argument("--prec", default="fp16", choices=["fp16", "bf16", "fp8"],
+                    help="custom workload: input precision (fp8 = OCP e4m3, bf16 output)")
+    ap.add_argument("--M", type=int, default=4096, help="custom workload: rows of A and C")
+    ap.add_argument("--N", type=int, default=4096, help="custom workload: columns of B and C")
+    ap.add_argument("--K-range", type=int, nargs=2, default=[128, 4096], metavar=("LO", "HI"),
+                    help="custom workload: K from LO to HI inclusive")
+    ap.add_argument("--K-step", type=int, default=128, help="custom workload: K step")
+    ap.add_argument("--grid-multiples", default="0",
+                    help="custom workload: comma-separated grid multiples of the persistent modes (0 = occupancy)")
+    ap.add_argument("--input", default="uniform", choices=["uniform", "normal"], help="custom workload: input values")
     ap.add_argument("--table", default=None, help="write the per-(K, mode) table as JSON here")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample duration")
@@ -174,6 +199,8 @@ def main():
     dev = torch.device("cuda:0")
     if args.workload == "uneven":
         return run_uneven(args, pg, si, torch, np)
+    if args.workload == "custom":
+        add_custom_workload(args)
     desc, dtype, kind, wid, probs = problems(args.workload)
     if args.modes:
         keep = {int(x) for x in args.modes.split(",")}

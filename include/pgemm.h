@@ -41,7 +41,8 @@ typedef enum {
   PGEMM_ERR_INVALID_ARG = 1, /* null pointer with non-zero size, negative size, bad enum */
   PGEMM_ERR_UNSUPPORTED = 2, /* size beyond the 32-bit tile/offset limits */
   PGEMM_ERR_HIP = 3,         /* a HIP runtime call failed; see pgemm_last_error() */
-  PGEMM_ERR_OOM = 4          /* device or host allocation failed */
+  PGEMM_ERR_OOM = 4,         /* device or host allocation failed */
+  PGEMM_ERR_TIMEOUT = 5      /* pgemm_wait: the stream's work did not finish in time */
 } pgemm_status_t;
 
 /* Element formats. The pages name fp16 and fp8 (Triton persistent-matmul
@@ -161,6 +162,16 @@ int pgemm_run(pgemm_handle_t h, const void* A, const void* B, void* C, int64_t M
  * workspace and the handle.
  * NULL is accepted (no-op). */
 int pgemm_destroy(pgemm_handle_t h);
+
+/* Watchdog wait: poll the handle's stream (hipStreamQuery, about every
+ * 50 microseconds) until all work enqueued on it has finished, or until
+ * timeout_ms milliseconds have passed. Returns PGEMM_OK when the stream is
+ * idle, PGEMM_ERR_TIMEOUT when the deadline passed first (the work keeps
+ * running; the caller may wait again), PGEMM_ERR_HIP if the stream reports
+ * an error (e.g. a kernel fault), PGEMM_ERR_INVALID_ARG for a NULL handle
+ * or a negative timeout. Lets a harness notice a kernel that never ends
+ * instead of blocking in a synchronize. */
+int pgemm_wait(pgemm_handle_t h, int timeout_ms);
 
 /* Static text for a status code. */
 const char* pgemm_status_string(int status);

@@ -19,6 +19,7 @@ PGEMM_ERR_INVALID_ARG = 1
 PGEMM_ERR_UNSUPPORTED = 2
 PGEMM_ERR_HIP = 3
 PGEMM_ERR_OOM = 4
+PGEMM_ERR_TIMEOUT = 5
 
 PGEMM_F16 = 0
 PGEMM_BF16 = 1
@@ -64,6 +65,7 @@ _set_tile_counter = _sig("pgemm_set_tile_counter", _int, _vp, _vp, _i64)
 _set_owner_log = _sig("pgemm_set_owner_log", _int, _vp, _vp, _i64)
 _set_tile_trace = _sig("pgemm_set_tile_trace", _int, _vp, _vp, _i64)
 _clock_khz = _sig("pgemm_clock_khz", _int, _int, _ip)
+_wait = _sig("pgemm_wait", _int, _vp, _int)
 _query_launch = _sig("pgemm_query_launch", _int, _vp, _i64, _i64, _i64, _int, _int, _int,
                      _ip, _ip, _ip, _ip, _ip, _ip, _ip)
 _query_streamk = _sig("pgemm_query_streamk", _int, _vp, _i64, _i64, _i64, _int, _int, _ip, _ip, _ip, _ip,
@@ -151,6 +153,11 @@ def pgemm_set_tile_trace(h, trace, n_tiles: int = 0) -> None:
     if trace is not None and not isinstance(trace, int) and not n_tiles:
         n_tiles = trace.numel() // 4
     _check(_set_tile_trace(h, _ptr(trace) or None, int(n_tiles)), h)
+
+
+def pgemm_wait(h, timeout_ms: int) -> None:
+    """Watchdog wait on the handle's stream; raises PgemmError(PGEMM_ERR_TIMEOUT) past the deadline."""
+    _check(_wait(h, int(timeout_ms)), h)
 
 
 def pgemm_clock_khz(device: int = 0) -> int:

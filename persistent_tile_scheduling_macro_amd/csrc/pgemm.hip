@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <chrono>
+#include <thread>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -378,6 +380,20 @@ int pgemm_destroy(pgemm_handle_t h) {
   return rc;
 }
 
+int pgemm_wait(pgemm_handle_t h, int timeout_ms) {
+  if (!h || timeout_ms < 0) return PGEMM_ERR_INVALID_ARG;
+  if (hipSetDevice(h->device) != hipSuccess) return fail(h, PGEMM_ERR_HIP, "hipSetDevice failed");
+  const auto deadline = std::chrono::steady_clock::now() + std::chrono::milliseconds(timeout_ms);
+  for (;;) {
+    const hipError_t e = hipStreamQuery(h->stream);
+    if (e == hipSuccess) return PGEMM_OK;
+    if (e != hipErrorNotReady) return fail(h, PGEMM_ERR_HIP, "stream query: %s", hipGetErrorString(e));
+    if (std::chrono::steady_clock::now() >= deadline)
+      return fail(h, PGEMM_ERR_TIMEOUT, "stream still busy after %d ms", timeout_ms);
+    std::this_thread::sleep_for(std::chrono::microseconds(50));
+  }
+}
+
 const char* pgemm_status_string(int status) {
   switch (status) {
     case PGEMM_OK: return "PGEMM_OK";
@@ -385,6 +401,7 @@ const char* pgemm_status_string(int status) {
     case PGEMM_ERR_UNSUPPORTED: return "PGEMM_ERR_UNSUPPORTED";
     case PGEMM_ERR_HIP: return "PGEMM_ERR_HIP";
     case PGEMM_ERR_OOM: return "PGEMM_ERR_OOM";
+    case PGEMM_ERR_TIMEOUT: return "PGEMM_ERR_TIMEOUT";
     default: return "PGEMM_ERR_UNKNOWN";
   }
 }

@@ -131,3 +131,14 @@ def test_tile_trace_argument_checks(pg):
     lib = ctypes.CDLL(pg.LIB_PATH)
     lib.pgemm_clock_khz.argtypes = [ctypes.c_int, ctypes.c_void_p]
     assert lib.pgemm_clock_khz(0, None) == pg.PGEMM_ERR_INVALID_ARG
+
+
+def test_wait_argument_checks(pg):
+    """The watchdog wait needs a handle and a non-negative deadline; its status has a name."""
+    with pytest.raises(pg.PgemmError) as e:
+        pg.pgemm_wait(None, 10)
+    assert e.value.status == pg.PGEMM_ERR_INVALID_ARG
+    assert pg.pgemm_status_string(pg.PGEMM_ERR_TIMEOUT) == "PGEMM_ERR_TIMEOUT"
+    text = open(HEADER).read()
+    m = re.search(r"PGEMM_ERR_TIMEOUT\s*=\s*(\d+)", text)
+    assert m and int(m.group(1)) == pg.PGEMM_ERR_TIMEOUT

@@ -24,3 +24,15 @@ def test_drain_with_no_events_inside_a_wave():
     en = np.array([100, 100, 100, 200, 200, 200, 300])
     assert bench.drain_start(st, en, 3, np) == 200
     assert bench.drain_start(st, en, 4, np) == 0  # never full: the drain is the whole run
+
+
+def test_custom_workload_from_flags(monkeypatch):
+    monkeypatch.setattr("sys.argv", ["bench.py", "--workload", "custom", "--prec", "bf16", "--M", "1000",
+                                     "--N", "2048", "--K-range", "256", "768", "--K-step", "256",
+                                     "--modes", "0,1", "--grid-multiples", "1,2"])
+    args = bench.parse()
+    bench.add_custom_workload(args)
+    desc, dtype, kind, wid, probs = bench.problems("custom")
+    assert dtype == "bf16" and kind == "uniform"
+    # the non-persistent mode ignores grid multiples; the persistent ones run each
+    assert probs == [(1000, 2048, K, m, g) for K in (256, 512, 768) for m, g in ((0, 0), (1, 1), (1, 2))]
