@@ -91,7 +91,10 @@ def test_workload_256_all_modes(pg, handle, dtype):
 
 
 SHAPES_INT = [(1, 1, 1), (7, 9, 5), (256, 256, 64), (300, 520, 200), (513, 264, 136), (64, 2048, 640),
-              (1, 784, 48), (259, 16, 1040)]
+              (1, 784, 48), (259, 16, 1040),
+              # odd and edge sizes: 17, 33, 127, 129, 255, 257 (unaligned: generic body), and the
+              # tail set's 4000 = 15*256 + 160 and 8200 = 32*256 + 8 in either dimension
+              (17, 33, 127), (129, 257, 255), (4000, 4000, 48), (8200, 264, 32), (264, 8200, 48)]
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16", "e4m3fn"])
@@ -131,10 +134,10 @@ def test_uniform_parity(pg, handle, dtype, shape):
 
 
 def test_brute_force_tiny(pg, handle):
-    """Every (M, N, K) in {1..6}^3, every mode, fp16 small integers: bit-exact."""
-    for M in range(1, 7):
-        for N in range(1, 7):
-            for K in range(1, 7):
+    """Every (M, N, K) in {1..9}^3, every mode, fp16 small integers: bit-exact."""
+    for M in range(1, 10):
+        for N in range(1, 10):
+            for K in range(1, 10):
                 A, B = si.operands(M, N, K, "f16", "small_int", workload=M * 100 + N * 10 + K)
                 want = oracle.round_to(oracle.gemm(si.bits(A), si.bits(B), "f16"), "f16")
                 for mode in MODES:
@@ -344,3 +347,47 @@ def test_size_limits_are_rejected_before_any_launch(pg):
         assert e.value.status == pg.PGEMM_ERR_UNSUPPORTED
     finally:
         pg.pgemm_destroy(h)
+
+
+def test_two_handles_on_two_streams_and_reruns(pg):
+    """Two handles, each bound to its own stream, run the claiming modes at the same time:
+    each handle's work counter serves only its own launches (every tile once per launch,
+    both counters back at 0), and ten back-to-back reruns per handle give the same bits."""
+    dev = torch.device("cuda:0")
+    probs = [(1000, 1032, 520, "f16"), (777, 1024, 264, "bf16")]
+    hs, streams, ins = [], [], []
+    for i, (M, N, K, dt) in enumerate(probs):
+        h = pg.pgemm_create(0)
+        st = torch.cuda.Stream()
+        pg.pgemm_set_stream(h, st)
+        pg.pgemm_set_tile_config(h, 2)  # 128 x 128: several tiles per persistent workgroup
+        A, B = si.operands(M, N, K, dt, "small_int", workload=30 + i)
+        ins.append((A.to(dev), B.to(dev), oracle.round_to(oracle.gemm(si.bits(A), si.bits(B), dt), dt)))
+        hs.append(h)
+        streams.append(st)
+    torch.cuda.synchronize()
+    try:
+        for mode in (2, 3):  # dynamic, cancel-and-reuse
+            say(f"case two handles mode {mode}")
+            outs, vis = [], []
+            for (M, N, K, dt), h, st, (A, B, _) in zip(probs, hs, streams, ins):
+                T = pg.pgemm_query_launch(h, M, N, K, DT[dt], mode, 0)["tiles"]
+                vis.append(torch.zeros((10, T), dtype=torch.int32, device=dev))
+                outs.append([torch.empty((M, N), dtype=OUT[dt][1], device=dev) for _ in range(10)])
+            # interleave the two handles' launches on their two streams
+            for r in range(10):
+                for i, ((M, N, K, dt), h) in enumerate(zip(probs, hs)):
+                    A, B, _ = ins[i]
+                    pg.pgemm_set_tile_counter(hs[i], vis[i][r])
+                    pg.pgemm_run(h, A, B, outs[i][r], M, N, K, DT[dt], mode, 0)
+            torch.cuda.synchronize()
+            for i, ((M, N, K, dt), h) in enumerate(zip(probs, hs)):
+                pg.pgemm_set_tile_counter(h, None)
+                assert (vis[i].cpu() == 1).all(), (mode, i)
+                assert pg.pgemm_read_work_counter(h) == 0
+                want = ins[i][2]
+                for r in range(10):
+                    assert np.array_equal(si.bits(outs[i][r].cpu()), want), (mode, i, r)
+    finally:
+        for h in hs:
+            pg.pgemm_destroy(h)
