@@ -101,6 +101,9 @@ def parse():
     ap.add_argument("--trace", action="store_true",
                     help="after timing, run every (problem, mode) once more with the tile trace on (untimed) and "
                          "report makespan, busy fraction of the workgroup slots and the drain (tail) time")
+    ap.add_argument("--trace-out", default=None, metavar="NPZ",
+                    help="with --trace: also save the raw traces (int64 [T, 4]: workgroup, XCD, start, end "
+                         "ticks; one array per problem and mode) and the clock rate to this .npz file")
     ap.add_argument("--tile", default="auto", choices=["auto", "256", "128"],
                     help="macro tile of the fast kernel (auto: the library's default choice)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -373,7 +376,7 @@ def main():
 
     trace_info = None
     if args.trace:
-        trace_info = tile_trace_summary(pg, h, probs, operands, outs, dt_code, torch, np)
+        trace_info = tile_trace_summary(pg, h, probs, operands, outs, dt_code, torch, np, args.trace_out)
 
     pg.pgemm_destroy(h)
 
@@ -425,7 +428,7 @@ def drain_start(st, en, slots, np):
     return int(ev[nxt, 0]) if nxt < len(ev) else int(en.max())
 
 
-def tile_trace_summary(pg, h, probs, operands, outs, dt_code, torch, np):
+def tile_trace_summary(pg, h, probs, operands, outs, dt_code, torch, np, raw_path=None):
     """One untimed run per (problem, mode) with the tile trace on. Per run:
     makespan (first tile start to last tile end), the busy fraction of the
     workgroup slots (CUs x occupancy) over the makespan, and the drain: the
@@ -437,6 +440,7 @@ def tile_trace_summary(pg, h, probs, operands, outs, dt_code, torch, np):
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     khz = pg.pgemm_clock_khz(0)
     out = {}
+    raw = {"clock_khz": np.array(khz)}
     for p in probs:
         m, n, K, mode, gm = p
         info = pg.pgemm_query_launch(h, m, n, K, dt_code, mode, gm)
@@ -451,6 +455,7 @@ def tile_trace_summary(pg, h, probs, operands, outs, dt_code, torch, np):
         finally:
             pg.pgemm_set_tile_trace(h, None)
         t = tr.view(T, 4).cpu().numpy()
+        raw[f"{m}x{n}x{K}_{MODE_NAMES[mode]}" + (f"_g{gm}" if gm else "")] = t
         wg, xcd, st, en = t[:, 0], t[:, 1], t[:, 2], t[:, 3]
         t0, t1 = int(st.min()), int(en.max())
         us = 1e3 / khz  # microseconds per tick
@@ -466,6 +471,8 @@ def tile_trace_summary(pg, h, probs, operands, outs, dt_code, torch, np):
             "tile_us_median": round(float(np.median(en - st)) * us, 1),
             "xcd_is_wg_mod_8": round(float((xcd[own] == wg[own] % 8).mean()), 4) if own.any() else None,
         }
+    if raw_path:
+        np.savez(raw_path, **raw)
     return out
 
 
@@ -519,6 +526,38 @@ def run_uneven(args, pg, si, torch, np):
             for m in order(s):
                 times[(hc, m)].append(one(hc, m))
     flops = 2.0 * M * N * K
+    trace_info = None
+    if args.trace:
+        # one untimed run per (held CUs, mode) with the tile trace on, the CUs held as above
+        khz = pg.pgemm_clock_khz(0)
+        trace_info, raw = {}, {"clock_khz": np.array(khz)}
+        for hc in held_set:
+            for m in modes:
+                T = pg.pgemm_query_launch(h, M, N, K, pg.PGEMM_F16, m, 0)["tiles"]
+                tr = torch.zeros(4 * T, dtype=torch.int64, device=dev)
+                pg.pgemm_set_tile_trace(h, tr)
+                try:
+                    one(hc, m)
+                finally:
+                    pg.pgemm_set_tile_trace(h, None)
+                t = tr.view(T, 4).cpu().numpy()
+                raw[f"held{hc}_{MODE_NAMES[m]}"] = t
+                wg, st, en = t[:, 0], t[:, 2], t[:, 3]
+                t0 = int(st.min())
+                us = 1e3 / khz
+                own = wg >= 0
+                per_wg = np.bincount(wg[own]) if own.any() else np.zeros(1, np.int64)
+                per_wg = per_wg[per_wg > 0]
+                first_start = {int(w): int(st[wg == w].min()) for w in np.unique(wg[own])}
+                trace_info.setdefault(f"held{hc}", {})[MODE_NAMES[m]] = {
+                    "makespan_us": round((int(en.max()) - t0) * us, 1),
+                    "workgroups_with_tiles": int(len(per_wg)),
+                    "tiles_per_wg_min": int(per_wg.min()), "tiles_per_wg_max": int(per_wg.max()),
+                    "last_first_start_us": round((max(first_start.values()) - t0) * us, 1) if first_start else None,
+                    "drain_us": round((int(en.max()) - drain_start(st, en, cus - hc, np)) * us, 1),
+                }
+        if args.trace_out:
+            np.savez(args.trace_out, **raw)
     table = []
     for (hc, m), ts in times.items():
         t = float(np.median(ts))
@@ -539,6 +578,8 @@ def run_uneven(args, pg, si, torch, np):
         "by_mode": {f"{r['mode']}@held{r['held_cus']}": r["tflops"] for r in table},
         "roofline": None, "cpu_baseline": None,
     }
+    if trace_info:
+        result["tile_trace"] = trace_info
     if args.table:
         with open(args.table, "w") as f:
             json.dump({"result": result, "table": table}, f, indent=1)
