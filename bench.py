@@ -104,6 +104,9 @@ def parse():
     ap.add_argument("--trace-out", default=None, metavar="NPZ",
                     help="with --trace: also save the raw traces (int64 [T, 4]: workgroup, XCD, start, end "
                          "ticks; one array per problem and mode) and the clock rate to this .npz file")
+    ap.add_argument("--b-layout", default="kn", choices=["kn", "nk"],
+                    help="storage of B: kn = K x N row-major (default, the configured workloads' layout), "
+                         "nk = N x K row-major (B transposed, as a linear layer stores its weight)")
     ap.add_argument("--tile", default="auto", choices=["auto", "256", "128"],
                     help="macro tile of the fast kernel (auto: the library's default choice)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -221,7 +224,8 @@ def main():
         A, B = si.operands(m, n, kmax, dtype, kind, workload=wid)
         Ad, Bd = A.to(dev), B.to(dev)
         for K in set(ks):
-            operands[(m, n, K)] = (Ad[:, :K].contiguous(), Bd[:K, :].contiguous())
+            Bk = Bd[:K, :]
+            operands[(m, n, K)] = (Ad[:, :K].contiguous(), Bk.t().contiguous() if args.b_layout == "nk" else Bk.contiguous())
         del A, B
     outs = {(m, n): torch.empty((m, n), dtype=out_dtype, device=dev) for (m, n) in shapes}
     torch.cuda.synchronize()
@@ -231,6 +235,7 @@ def main():
     pg.pgemm_set_stream(h, stream)
     pg.pgemm_set_tile_config(h, {"auto": pg.PGEMM_TILE_AUTO, "256": pg.PGEMM_TILE_256,
                                  "128": pg.PGEMM_TILE_128}[args.tile])
+    pg.pgemm_set_b_layout(h, pg.PGEMM_B_NK if args.b_layout == "nk" else pg.PGEMM_B_KN)
 
     def launch(p):
         m, n, K, mode, gm = p
@@ -389,7 +394,8 @@ def main():
         "value": round(value, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(wall / args.steps * 1e3, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": dtype if dtype != "e4m3fn" else "e4m3fn->bf16", "data": "synthetic",
-        "config": {"workload": desc, "name": args.workload, "tile": args.tile, "launches_per_step": len(probs),
+        "config": {"workload": desc, "name": args.workload, "tile": args.tile, "b_layout": args.b_layout,
+                   "launches_per_step": len(probs),
                    "flops_per_step": step_flops},
         "frac_of_peak": round(value / peak, 4),
         "mode_tflops": mode_tflops,

@@ -8,8 +8,10 @@
  * The operation (persistent-kernel forum thread, question): the GEMM
  *     C[i][j] = sum_k A[i][k] * B[k][j]
  * with A: M x K row-major (leading dimension K), B: K x N row-major
- * (leading dimension N), C: M x N row-major (leading dimension N), all
- * contiguous, accumulated in fp32. The output is cut into macro tiles and
+ * (leading dimension N) -- or, after pgemm_set_b_layout(h, PGEMM_B_NK),
+ * N x K row-major (leading dimension K, i.e. B stored transposed, the layout
+ * of a linear layer's weight) -- and C: M x N row-major (leading dimension
+ * N), all contiguous, accumulated in fp32. The output is cut into macro tiles and
  * a tile scheduler hands tiles to workgroups (same question). Scheduling
  * never changes the value of C: modes NONPERSISTENT..CANCEL run the same
  * tile body, so C is bitwise identical across them and across reruns
@@ -117,6 +119,14 @@ typedef enum {
   PGEMM_TILE_256 = 1,
   PGEMM_TILE_128 = 2
 } pgemm_tile_t;
+
+/* Storage of B (pgemm_set_b_layout). The value of C does not depend on it:
+ * both layouts feed the MFMAs the same operands in the same order, so C is
+ * bitwise the same. */
+typedef enum {
+  PGEMM_B_KN = 0, /* B[k][n] at B + k*N + n (default) */
+  PGEMM_B_NK = 1  /* B[k][n] at B + n*K + k */
+} pgemm_b_layout_t;
 
 /* Create a handle on HIP device `device` (which becomes current). Allocates
  * the claiming modes' device work counter (zeroed) and caches the CU count.
@@ -255,6 +265,14 @@ int pgemm_set_tile_order(pgemm_handle_t h, int group_m, int xcd_remap);
  * (pgemm_tile_t). Unaligned operands always take the generic 64 x 64 body.
  * Returns PGEMM_ERR_INVALID_ARG for an unknown value. */
 int pgemm_set_tile_config(pgemm_handle_t h, int tile);
+
+/* Choose how B is stored for later runs on this handle (pgemm_b_layout_t;
+ * default PGEMM_B_KN). With PGEMM_B_NK the fast kernel copies B's tile like
+ * A's (rows of 128 bytes) and reads its fragments with plain 16-byte LDS
+ * reads instead of LDS transpose reads. The fast-kernel size rule is the
+ * same in both layouts (K and N multiples of 16 bytes of elements).
+ * Returns PGEMM_ERR_INVALID_ARG for a NULL handle or an unknown value. */
+int pgemm_set_b_layout(pgemm_handle_t h, int layout);
 
 /* Host mirror of the device tile order: (pid_m, pid_n) of tile t for an
  * n_m x n_n tile grid, with the same knobs and CU-count chunking the

@@ -35,6 +35,9 @@ PGEMM_TILE_AUTO = 0
 PGEMM_TILE_256 = 1
 PGEMM_TILE_128 = 2
 
+PGEMM_B_KN = 0
+PGEMM_B_NK = 1
+
 DTYPE_NAMES = {"f16": PGEMM_F16, "bf16": PGEMM_BF16, "e4m3fn": PGEMM_F8E4M3_BF16}
 SCHED_NAMES = {"nonpersistent": PGEMM_SCHED_NONPERSISTENT, "static": PGEMM_SCHED_STATIC,
                "dynamic": PGEMM_SCHED_DYNAMIC, "cancel": PGEMM_SCHED_CANCEL, "streamk": PGEMM_SCHED_STREAMK}
@@ -72,6 +75,7 @@ _query_streamk = _sig("pgemm_query_streamk", _int, _vp, _i64, _i64, _i64, _int, 
                       ctypes.POINTER(_i64))
 _set_tile_order = _sig("pgemm_set_tile_order", _int, _vp, _int, _int)
 _set_tile_config = _sig("pgemm_set_tile_config", _int, _vp, _int)
+_set_b_layout = _sig("pgemm_set_b_layout", _int, _vp, _int)
 _tile_coords = _sig("pgemm_tile_coords", _int, _i64, _i64, _i64, _int, _int, _ip, _ip)
 _read_work_counter = _sig("pgemm_read_work_counter", _int, _vp, ctypes.POINTER(_i32))
 _hold_cus = _sig("pgemm_hold_cus", _int, _vp, _int, _int, _int)
@@ -196,6 +200,11 @@ def pgemm_set_tile_order(h, group_m: int = 8, xcd_remap=True) -> None:
 
 def pgemm_set_tile_config(h, tile: int) -> None:
     _check(_set_tile_config(h, int(tile)), h)
+
+
+def pgemm_set_b_layout(h, layout: int) -> None:
+    """PGEMM_B_KN: B is K x N row-major (default); PGEMM_B_NK: B is N x K row-major."""
+    _check(_set_b_layout(h, int(layout)), h)
 
 
 def pgemm_tile_coords(t: int, n_m: int, n_n: int, group_m: int = 8, cu_chunk: int = 0):

@@ -176,8 +176,13 @@ __device__ inline typename Frag<DT>::t read_a(const uint8_t* lo, const uint8_t* 
 
 // TRACE selects the instantiation that writes the tile trace (p.trace); the
 // timed kernels carry no trace code at all, so their register allocation is
-// untouched by it.
-template <int DT, int SCHED, int CFG, bool TRACE>
+// untouched by it. BT selects B given as N x K row-major (K contiguous, the
+// layout of a linear layer's weight): B's tile is then copied and swizzled
+// exactly like A's (BN rows of 128 bytes), and its fragments are plain
+// 16-byte reads instead of LDS transpose reads. Each lane reads the B row
+// that the permuted column order gives its n-position, so the MFMAs see the
+// same operands as with K x N B and C is bitwise the same.
+template <int DT, int SCHED, int CFG, bool TRACE, bool BT>
 __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, Tile<CFG>::MIN_WAVES_PER_SIMD) gemm_fast_kernel(Params p) {
   constexpr int BM = Tile<CFG>::BM, BN = Tile<CFG>::BN;
   constexpr int WAVES = Tile<CFG>::WAVES, THREADS = WAVES * 64;
@@ -229,7 +234,7 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, Tile<CFG>::MIN_WAVES_PE
   // 0 (an extra step reads zeros: it lies past K)
   const int nk = ((K + BK - 1) / BK + 1) & ~1;
   const int64_t lda = (int64_t)K * ES; // bytes per row of A
-  const int64_t ldb = (int64_t)N * ES; // bytes per row of B
+  const int64_t ldb = BT ? (int64_t)K * ES : (int64_t)N * ES; // bytes per row of B (or of N x K B)
   const int64_t ldc = N;               // elements per row of C
 
   // ---- per-lane constants of the global -> LDS copy ------------------------
@@ -273,6 +278,19 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, Tile<CFG>::MIN_WAVES_PE
   int b_off[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
+    if constexpr (BT) {
+      // N x K B: this lane's B row is the wave column of its n-position s16
+      // (16-bit: the permuted order below; fp8: plain), stored like an A row
+      if constexpr (ES == 2) {
+        const int q = s16 >> 2;
+        const int r = wn * WN + 32 * (nb >> 1) + 8 * q + 4 * ((nb + q) & 1) + (s16 & 3);
+        b_off[nb] = r * A_ROW + 16 * (g ^ (r & 7)); // k-group 1: chunk 4 + g, i.e. offset ^ 64
+      } else {
+        const int r = wn * WN + nb * 16 + s16;
+        b_off[nb] = r * A_ROW + 16 * ((2 * g) ^ (((r >> 1) & 1) | (r & 4))); // second chunk: ^ 16
+      }
+      continue;
+    }
     // the swizzle is the same for every row this lane reads from here
     // (+4 and +32 rows for 16-bit, +8/+16/+24 for fp8)
     if constexpr (ES == 2) {
@@ -369,10 +387,10 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, Tile<CFG>::MIN_WAVES_PE
     // A rebased at (m0, k0), B at (k0, n0); rows past M or K and chunks past
     // K or N read zeros.
     ra = make_rsrc(p.A + (int64_t)m0 * lda + (int64_t)k0 * ES);
-    rb = make_rsrc(p.B + (int64_t)k0 * ldb + (int64_t)n0 * ES);
+    rb = BT ? make_rsrc(p.B + (int64_t)n0 * ldb + (int64_t)k0 * ES) : make_rsrc(p.B + (int64_t)k0 * ldb + (int64_t)n0 * ES);
     p_mrem = M - m0;
     p_krem = K - k0;
-    p_nrem = (N - n0) * ES;
+    p_nrem = BT ? N - n0 : (N - n0) * ES; // BT: rows of N x K B left
     p_kval = (k0 * ES + 16 * a_chunk) < K * ES;
     p_busy = true;
     ++issued;
@@ -386,11 +404,19 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, Tile<CFG>::MIN_WAVES_PE
       load16_to_lds(ra, sA + (wave + WAVES * J) * 1024, off);
     } else {
       constexpr int JB = J - LA;
-      const int row = b_row0 + B_RPI * WAVES * JB;
-      const int Lc = b_chunk0 ^ b_swz<ES, B_ROW>(B_RPI * WAVES * JB);
-      const bool ok = (row < p_krem) & (16 * Lc < p_nrem);
-      const uint32_t off = ok ? (uint32_t)row * (uint32_t)ldb + 16u * (uint32_t)Lc : kOOB;
-      load16_to_lds(rb, sB + (wave + WAVES * JB) * 1024, off);
+      if constexpr (BT) {
+        // rows n of N x K B, copied like A's rows m (same lanes, chunks and swizzle)
+        const bool ok = p_kval & (a_row0 + 8 * WAVES * JB < p_nrem);
+        const uint32_t off = ok ? ((uint32_t)a_row0 + (uint32_t)(8 * WAVES * JB)) * (uint32_t)ldb + 16u * (uint32_t)a_chunk
+                                : kOOB;
+        load16_to_lds(rb, sB + (wave + WAVES * JB) * 1024, off);
+      } else {
+        const int row = b_row0 + B_RPI * WAVES * JB;
+        const int Lc = b_chunk0 ^ b_swz<ES, B_ROW>(B_RPI * WAVES * JB);
+        const bool ok = (row < p_krem) & (16 * Lc < p_nrem);
+        const uint32_t off = ok ? (uint32_t)row * (uint32_t)ldb + 16u * (uint32_t)Lc : kOOB;
+        load16_to_lds(rb, sB + (wave + WAVES * JB) * 1024, off);
+      }
     }
     if (J == L - 1) p_busy = false;
   };
@@ -416,7 +442,14 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, Tile<CFG>::MIN_WAVES_PE
   };
   auto read_b_frag = [&](auto f, const uint8_t* sB, int kk, int nb) __attribute__((always_inline)) {
     constexpr int F = decltype(f)::value;
-    bf[F][nb] = read_b<DT, B_ROW>(sB + b_off[nb] + kk * 32 * B_ROW);
+    if constexpr (BT) {
+      if constexpr (ES == 2)
+        bf[F][nb] = read_a<DT>(sB + (b_off[nb] ^ (64 * kk)), nullptr);
+      else
+        bf[F][nb] = read_a<DT>(sB + b_off[nb], sB + (b_off[nb] ^ 16));
+    } else {
+      bf[F][nb] = read_b<DT, B_ROW>(sB + b_off[nb] + kk * 32 * B_ROW);
+    }
   };
   auto mfma_row = [&](auto f, int mb) __attribute__((always_inline)) {
     constexpr int F = decltype(f)::value;

@@ -70,7 +70,7 @@ __global__ void __launch_bounds__(THREADS) gemm_generic_kernel(Params p) {
       for (int e = tid; e < BN * KG; e += THREADS) {
         const int k = e / BN, c = e % BN;
         const int gk = k0 + k, gn = n0 + c;
-        elem_t v = (gk < p.K && gn < p.N) ? B[(int64_t)gk * p.N + gn] : (elem_t)0;
+        elem_t v = (gk < p.K && gn < p.N) ? B[p.b_nk ? (int64_t)gn * p.K + gk : (int64_t)gk * p.N + gn] : (elem_t)0;
         *reinterpret_cast<elem_t*>(sB + c * ROWB + k * ES) = v;
       }
       __syncthreads();

@@ -12,10 +12,11 @@ typedef void (*kernel_fn)(Params);
 enum Body : int { kBodyGeneric = 0, kBodyTile256 = 1, kBodyTile128 = 2 };
 
 // Returns the kernel for (scheduling mode, tile body); `trace` selects the
-// fast bodies' instantiation that writes the tile trace.
-kernel_fn pick_kernel_f16(int sched, int body, bool trace);
-kernel_fn pick_kernel_bf16(int sched, int body, bool trace);
-kernel_fn pick_kernel_f8(int sched, int body, bool trace);
+// fast bodies' instantiation that writes the tile trace, `bt` the one that
+// takes B as N x K (the generic body reads Params::b_nk instead).
+kernel_fn pick_kernel_f16(int sched, int body, bool trace, bool bt);
+kernel_fn pick_kernel_bf16(int sched, int body, bool trace, bool bt);
+kernel_fn pick_kernel_f8(int sched, int body, bool trace, bool bt);
 
 // The stream-K fix-up kernel of a fast tile body (nullptr for the generic body).
 kernel_fn pick_fixup_f16(int body);

@@ -3,7 +3,9 @@
 
 namespace pgemm {
 
-kernel_fn pick_kernel_bf16(int sched, int body, bool trace) { return pick_for_dtype<kBF16>(sched, body, trace); }
+kernel_fn pick_kernel_bf16(int sched, int body, bool trace, bool bt) {
+  return pick_for_dtype<kBF16>(sched, body, trace, bt);
+}
 kernel_fn pick_fixup_bf16(int body) { return pick_fixup_for_dtype<kBF16>(body); }
 
 } // namespace pgemm

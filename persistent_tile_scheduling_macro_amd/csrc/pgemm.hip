@@ -28,6 +28,7 @@ struct pgemm_ctx {
   int64_t n_owner = 0;
   int64_t* trace = nullptr;
   int64_t n_trace = 0;
+  int b_nk = 0; // layout of B: 0 = K x N row-major, 1 = N x K row-major
   // Tile-order defaults measured on MI355X (8192^3 and 4096^3 fp16, round-robin
   // timing): GROUP_SIZE_M between 1 and 16 moved throughput by a few percent
   // at most. The XCD remap (-1 = automatic: on when a launch has more tiles
@@ -73,11 +74,11 @@ BodyShape body_shape(int body) {
 }
 int fast_block_k(int dtype) { return dtype == kF8E4M3 ? 128 : 64; }
 
-kernel_fn pick_kernel(int dtype, int sched, int body, bool trace = false) {
+kernel_fn pick_kernel(int dtype, int sched, int body, bool trace = false, bool bt = false) {
   switch (dtype) {
-    case kF16: return pick_kernel_f16(sched, body, trace);
-    case kBF16: return pick_kernel_bf16(sched, body, trace);
-    default: return pick_kernel_f8(sched, body, trace);
+    case kF16: return pick_kernel_f16(sched, body, trace, bt);
+    case kBF16: return pick_kernel_bf16(sched, body, trace, bt);
+    default: return pick_kernel_f8(sched, body, trace, bt);
   }
 }
 
@@ -303,6 +304,7 @@ int pgemm_run(pgemm_handle_t h, const void* A, const void* B, void* C, int64_t M
   p.visits = h->visits;
   p.owner = h->owner;
   p.trace = reinterpret_cast<long long*>(h->trace);
+  p.b_nk = h->b_nk;
   p.sk_waves = pl.sk_waves;
   p.sk_tiles = pl.sk_tiles;
   p.sk_groups = pl.sk_groups;
@@ -324,7 +326,7 @@ int pgemm_run(pgemm_handle_t h, const void* A, const void* B, void* C, int64_t M
     p.work = h->work;
   }
   if (sched_mode != kStreamK || !pl.fast) {
-    kernel_fn k = pick_kernel(dtype, sched_mode, pl.body, p.trace != nullptr);
+    kernel_fn k = pick_kernel(dtype, sched_mode, pl.body, p.trace != nullptr, p.b_nk != 0);
     hipLaunchKernelGGL(k, dim3((unsigned)pl.G), dim3(pl.threads), 0, h->stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(h, PGEMM_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
@@ -344,8 +346,8 @@ int pgemm_run(pgemm_handle_t h, const void* A, const void* B, void* C, int64_t M
     pd.T = (int)(pl.T - pl.sk_tiles); // W * G
     pd.sk_waves = pd.sk_tiles = pd.sk_groups = 0;
     pd.work = nullptr;
-    hipLaunchKernelGGL(pick_kernel(dtype, kStatic, pl.body, p.trace != nullptr), dim3((unsigned)pl.G), dim3(pl.threads), 0,
-                       h->stream, pd);
+    hipLaunchKernelGGL(pick_kernel(dtype, kStatic, pl.body, p.trace != nullptr, p.b_nk != 0), dim3((unsigned)pl.G),
+                       dim3(pl.threads), 0, h->stream, pd);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(h, PGEMM_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
   }
@@ -353,8 +355,8 @@ int pgemm_run(pgemm_handle_t h, const void* A, const void* B, void* C, int64_t M
     Params ps = p;
     ps.sk_waves = 0;
     ps.G = pl.sk_groups;
-    hipLaunchKernelGGL(pick_kernel(dtype, kStreamK, pl.body, p.trace != nullptr), dim3((unsigned)pl.sk_groups),
-                       dim3(pl.threads), 0, h->stream, ps);
+    hipLaunchKernelGGL(pick_kernel(dtype, kStreamK, pl.body, p.trace != nullptr, p.b_nk != 0),
+                       dim3((unsigned)pl.sk_groups), dim3(pl.threads), 0, h->stream, ps);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(h, PGEMM_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
     if (pl.sk_split) {
@@ -429,6 +431,13 @@ int pgemm_set_tile_trace(pgemm_handle_t h, int64_t* dev_trace, int64_t n_tiles) 
   if (dev_trace && n_tiles <= 0) return fail(h, PGEMM_ERR_INVALID_ARG, "n_tiles must be positive");
   h->trace = dev_trace;
   h->n_trace = dev_trace ? n_tiles : 0;
+  return PGEMM_OK;
+}
+
+int pgemm_set_b_layout(pgemm_handle_t h, int layout) {
+  if (!h) return PGEMM_ERR_INVALID_ARG;
+  if (layout != PGEMM_B_KN && layout != PGEMM_B_NK) return fail(h, PGEMM_ERR_INVALID_ARG, "unknown B layout %d", layout);
+  h->b_nk = layout == PGEMM_B_NK;
   return PGEMM_OK;
 }
 

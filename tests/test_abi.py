@@ -142,3 +142,14 @@ def test_wait_argument_checks(pg):
     text = open(HEADER).read()
     m = re.search(r"PGEMM_ERR_TIMEOUT\s*=\s*(\d+)", text)
     assert m and int(m.group(1)) == pg.PGEMM_ERR_TIMEOUT
+
+
+def test_b_layout_argument_checks(pg):
+    """The B-layout setter needs a handle; the layout constants match the header."""
+    with pytest.raises(pg.PgemmError) as e:
+        pg.pgemm_set_b_layout(None, pg.PGEMM_B_NK)
+    assert e.value.status == pg.PGEMM_ERR_INVALID_ARG
+    text = open(HEADER).read()
+    for name in ("PGEMM_B_KN", "PGEMM_B_NK"):
+        m = re.search(name + r"\s*=\s*(\d+)", text)
+        assert m and int(m.group(1)) == getattr(pg, name)
