@@ -50,7 +50,8 @@ typedef enum {
 /* Element formats. The pages name fp16 and fp8 (Triton persistent-matmul
  * issue: "--prec fp16", and the fp8 example on H100); bf16 is the other
  * 16-bit format of the same MFMA family. fp8 is OCP E4M3 ("fn": bias 7,
- * max 448, no infinities) with a per-tensor scale of 1.0. */
+ * max 448, no infinities) with a per-tensor scale for each of A and B: 1.0
+ * by default, any finite value through pgemm_set_fp8_scales. */
 typedef enum {
   PGEMM_F16 = 0,         /* A, B, C: IEEE binary16 */
   PGEMM_BF16 = 1,        /* A, B, C: bfloat16 */
@@ -265,6 +266,16 @@ int pgemm_set_tile_order(pgemm_handle_t h, int group_m, int xcd_remap);
  * (pgemm_tile_t). Unaligned operands always take the generic 64 x 64 body.
  * Returns PGEMM_ERR_INVALID_ARG for an unknown value. */
 int pgemm_set_tile_config(pgemm_handle_t h, int tile);
+
+/* Per-tensor scales of e4m3 A and B for later PGEMM_F8E4M3_BF16 runs on this
+ * handle: the stored codes represent scale_a * dec(a) and scale_b * dec(b),
+ * so C[i][j] = scale_a * scale_b * sum_k dec(A[i][k]) * dec(B[k][j]). The
+ * epilogue multiplies the fp32 sum by the fp32 product scale_a * scale_b and
+ * rounds to bf16 (nearest-even); with power-of-two scales that product and
+ * multiplication are exact. Default 1.0 and 1.0 (exact: C unchanged). Other
+ * dtypes ignore the scales. PGEMM_ERR_INVALID_ARG for a NULL handle, a
+ * non-finite scale or a non-finite product. */
+int pgemm_set_fp8_scales(pgemm_handle_t h, float scale_a, float scale_b);
 
 /* Choose how B is stored for later runs on this handle (pgemm_b_layout_t;
  * default PGEMM_B_KN). With PGEMM_B_NK the fast kernel copies B's tile like

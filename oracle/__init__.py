@@ -13,7 +13,9 @@ and CLC scheduling": scheduling adds no work and changes no value):
     C[i, j] = sum_k dec(A[i, k]) * dec(B[k, j])      in IEEE double, k ascending
 
 with A (M x K), B (K x N), C (M x N) row-major and dec() the exact decoding
-of IEEE binary16, bfloat16 or OCP E4M3 ("fn") bit patterns.
+of IEEE binary16, bfloat16 or OCP E4M3 ("fn") bit patterns. Quantised e4m3
+inputs with per-tensor scales sA, sB represent sA * dec(a) and sB * dec(b),
+so their C is sA * sB times that sum.
 """
 from __future__ import annotations
 
@@ -119,8 +121,14 @@ def round_to(x: np.ndarray, out_dtype: str) -> np.ndarray:
     return out
 
 
-def gemm(A_bits: np.ndarray, B_bits: np.ndarray, dtype: str, rows=None, nthreads=None) -> np.ndarray:
-    """fp64 C = dec(A) @ dec(B); with `rows`, only those rows of C (in that order)."""
+def gemm(A_bits: np.ndarray, B_bits: np.ndarray, dtype: str, rows=None, nthreads=None,
+         scale_a: float = 1.0, scale_b: float = 1.0) -> np.ndarray:
+    """fp64 C = dec(A) @ dec(B); with `rows`, only those rows of C (in that order).
+
+    scale_a, scale_b: per-tensor scales of quantised inputs (the e4m3 workload's
+    dequantisation, value = scale * decoded code). A scaled code times a scaled
+    code is the two scales times the product of the codes, so the scaled sum is
+    scale_a * scale_b times the unscaled one, applied here in double."""
     A = _bits(A_bits, dtype)
     B = _bits(B_bits, dtype)
     if A.ndim != 2 or B.ndim != 2 or A.shape[1] != B.shape[0]:
@@ -139,6 +147,8 @@ def gemm(A_bits: np.ndarray, B_bits: np.ndarray, dtype: str, rows=None, nthreads
                                   r.ctypes.data, r.size, _dptr(C), nt)
     if rc:
         raise RuntimeError(f"oracle gemm failed ({rc})")
+    if scale_a != 1.0 or scale_b != 1.0:
+        C *= float(scale_a) * float(scale_b)
     return C
 
 

@@ -76,6 +76,7 @@ _query_streamk = _sig("pgemm_query_streamk", _int, _vp, _i64, _i64, _i64, _int, 
 _set_tile_order = _sig("pgemm_set_tile_order", _int, _vp, _int, _int)
 _set_tile_config = _sig("pgemm_set_tile_config", _int, _vp, _int)
 _set_b_layout = _sig("pgemm_set_b_layout", _int, _vp, _int)
+_set_fp8_scales = _sig("pgemm_set_fp8_scales", _int, _vp, ctypes.c_float, ctypes.c_float)
 _tile_coords = _sig("pgemm_tile_coords", _int, _i64, _i64, _i64, _int, _int, _ip, _ip)
 _read_work_counter = _sig("pgemm_read_work_counter", _int, _vp, ctypes.POINTER(_i32))
 _hold_cus = _sig("pgemm_hold_cus", _int, _vp, _int, _int, _int)
@@ -200,6 +201,11 @@ def pgemm_set_tile_order(h, group_m: int = 8, xcd_remap=True) -> None:
 
 def pgemm_set_tile_config(h, tile: int) -> None:
     _check(_set_tile_config(h, int(tile)), h)
+
+
+def pgemm_set_fp8_scales(h, scale_a: float, scale_b: float) -> None:
+    """Per-tensor scales of e4m3 A and B (C = scale_a * scale_b * sum of decoded products)."""
+    _check(_set_fp8_scales(h, float(scale_a), float(scale_b)), h)
 
 
 def pgemm_set_b_layout(h, layout: int) -> None:

@@ -68,6 +68,7 @@ struct Params {
   int* owner;      // optional int32[T] owner log (workgroup id per tile)
   long long* trace; // optional int64[4T] tile trace {workgroup, XCD, start, end}
   int b_nk;         // 1: B is N x K row-major (K contiguous); 0: K x N row-major
+  float c_scale;    // e4m3 inputs: product of the per-tensor scales of A and B (else 1)
   // stream-K only (zero otherwise): the first T - sk_tiles tiles run whole,
   // sk_waves per workgroup; the k-step pairs of the last sk_tiles tiles are
   // split over workgroups 0 .. sk_groups-1; pieces that do not cover their

@@ -499,6 +499,8 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, Tile<CFG>::MIN_WAVES_PE
         }
       }
     } else {
+      // e4m3 inputs: dequantise the sum with the product of the per-tensor scales
+      const float cs = p.c_scale;
       const int ncol = pn * BN + wn * WN + 4 * g;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
@@ -509,11 +511,11 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, Tile<CFG>::MIN_WAVES_PE
             const int n = ncol + nb * 16;
             out_t* dst = C + (int64_t)m * ldc + n;
             if (n + 3 < N) {
-              store4(dst, acc_read(acc[mb][nb]));
+              store4(dst, acc_read(acc[mb][nb]) * cs);
             } else {
 #pragma unroll
               for (int e = 0; e < 4; ++e)
-                if (n + e < N) dst[e] = to_out(acc[mb][nb][e], (out_t*)nullptr);
+                if (n + e < N) dst[e] = to_out(acc[mb][nb][e] * cs, (out_t*)nullptr);
             }
           }
         }
@@ -733,6 +735,10 @@ __global__ void __launch_bounds__(256) sk_fixup_kernel(Params p) {
       src += (int64_t)BM * BN;
       lo += *reinterpret_cast<const floatx4_t*>(src);
       hi += *reinterpret_cast<const floatx4_t*>(src + 4);
+    }
+    if constexpr (ES == 1) { // e4m3 inputs: the partials are unscaled sums
+      lo *= p.c_scale;
+      hi *= p.c_scale;
     }
     store8(reinterpret_cast<out_t*>(p.C) + (int64_t)m * p.N + n, lo, hi, false);
   }

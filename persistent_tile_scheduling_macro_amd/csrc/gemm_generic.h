@@ -105,7 +105,8 @@ __global__ void __launch_bounds__(THREADS) gemm_generic_kernel(Params p) {
       for (int j = 0; j < 2; ++j) {
         const int n = n0 + wn * 32 + j * 16 + 4 * g;
         for (int e = 0; e < 4; ++e)
-          if (n + e < p.N) C[(int64_t)m * p.N + n + e] = to_out(acc[i][j][e], (out_t*)nullptr);
+          if (n + e < p.N)
+            C[(int64_t)m * p.N + n + e] = to_out(ES == 1 ? acc[i][j][e] * p.c_scale : acc[i][j][e], (out_t*)nullptr);
       }
     }
     if (tid == 0) {

@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <chrono>
+#include <cmath>
 #include <thread>
 #include <cstdarg>
 #include <cstdio>
@@ -29,6 +30,7 @@ struct pgemm_ctx {
   int64_t* trace = nullptr;
   int64_t n_trace = 0;
   int b_nk = 0; // layout of B: 0 = K x N row-major, 1 = N x K row-major
+  float scale_a = 1.0f, scale_b = 1.0f; // per-tensor scales of e4m3 A and B
   // Tile-order defaults measured on MI355X (8192^3 and 4096^3 fp16, round-robin
   // timing): GROUP_SIZE_M between 1 and 16 moved throughput by a few percent
   // at most. The XCD remap (-1 = automatic: on when a launch has more tiles
@@ -305,6 +307,7 @@ int pgemm_run(pgemm_handle_t h, const void* A, const void* B, void* C, int64_t M
   p.owner = h->owner;
   p.trace = reinterpret_cast<long long*>(h->trace);
   p.b_nk = h->b_nk;
+  p.c_scale = dtype == kF8E4M3 ? h->scale_a * h->scale_b : 1.0f;
   p.sk_waves = pl.sk_waves;
   p.sk_tiles = pl.sk_tiles;
   p.sk_groups = pl.sk_groups;
@@ -438,6 +441,15 @@ int pgemm_set_b_layout(pgemm_handle_t h, int layout) {
   if (!h) return PGEMM_ERR_INVALID_ARG;
   if (layout != PGEMM_B_KN && layout != PGEMM_B_NK) return fail(h, PGEMM_ERR_INVALID_ARG, "unknown B layout %d", layout);
   h->b_nk = layout == PGEMM_B_NK;
+  return PGEMM_OK;
+}
+
+int pgemm_set_fp8_scales(pgemm_handle_t h, float scale_a, float scale_b) {
+  if (!h) return PGEMM_ERR_INVALID_ARG;
+  if (!std::isfinite(scale_a) || !std::isfinite(scale_b) || !std::isfinite(scale_a * scale_b))
+    return fail(h, PGEMM_ERR_INVALID_ARG, "fp8 scales must be finite with a finite product");
+  h->scale_a = scale_a;
+  h->scale_b = scale_b;
   return PGEMM_OK;
 }
 

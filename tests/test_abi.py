@@ -153,3 +153,10 @@ def test_b_layout_argument_checks(pg):
     for name in ("PGEMM_B_KN", "PGEMM_B_NK"):
         m = re.search(name + r"\s*=\s*(\d+)", text)
         assert m and int(m.group(1)) == getattr(pg, name)
+
+
+def test_fp8_scales_argument_checks(pg):
+    """The fp8 scale setter needs a handle (no device is touched on the failure path)."""
+    with pytest.raises(pg.PgemmError) as e:
+        pg.pgemm_set_fp8_scales(None, 1.0, 1.0)
+    assert e.value.status == pg.PGEMM_ERR_INVALID_ARG

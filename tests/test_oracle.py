@@ -222,6 +222,25 @@ def test_gemm_small_integers_match_int64_matmul(dtype):
     assert np.array_equal(got, ref.astype(np.float64))
 
 
+def test_gemm_scaled_e4m3_matches_exact_rational_dequantisation():
+    """Per-tensor scales: each scaled code is scale * code, so C is the exact
+    rational sum of (sA * a) * (sB * b); checked with fractions on small integers
+    (exact in double), for power-of-two and general scales, rows included."""
+    M, N, K = 7, 5, 19
+    A, B = si.operands(M, N, K, "e4m3fn", "small_int", workload=9)
+    a = A.to(torch.int64).numpy()
+    b = B.to(torch.int64).numpy()
+    for sa, sb in [(0.5, 4.0), (0.25, 0.125), (0.37, 1.9), (-3.0, 0.75)]:
+        got = oracle.gemm(si.bits(A), si.bits(B), "e4m3fn", scale_a=sa, scale_b=sb)
+        for i in range(M):
+            for j in range(N):
+                exact = sum(Fraction(sa) * int(a[i, k]) * Fraction(sb) * int(b[k, j]) for k in range(K))
+                assert abs(Fraction(got[i, j]) - exact) <= abs(exact) * Fraction(1, 2 ** 50), (sa, sb, i, j)
+        rows = [4, 0, 6]
+        assert np.array_equal(oracle.gemm(si.bits(A), si.bits(B), "e4m3fn", rows=rows, scale_a=sa, scale_b=sb),
+                              got[rows])
+
+
 def test_gemm_rows_and_threads():
     M, N, K = 50, 33, 70
     A, B = si.operands(M, N, K, "f16", "uniform", workload=9)
