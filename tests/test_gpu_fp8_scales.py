@@ -113,3 +113,33 @@ def test_non_finite_scales_rejected(pg, handle):
         with pytest.raises(pg.PgemmError) as e:
             pg.pgemm_set_fp8_scales(handle, sa, sb)
         assert e.value.status == pg.PGEMM_ERR_INVALID_ARG
+
+
+def test_scales_with_nk_layout_and_trace(pg, handle):
+    """The features together: e4m3 with B stored N x K, power-of-two scales and the tile
+    trace (its own kernel instantiation) -- bit-exact on small integers in every mode,
+    and every tile traced once with start <= end."""
+    M, N, K = 1000, 1008, 4000  # ragged edges; long K (stream-K splits at the 128 tile)
+    sa, sb = 0.5, 2.0
+    A, B = si.operands(M, N, K, "e4m3fn", "small_int", workload=53)
+    want = oracle.round_to(oracle.gemm(si.bits(A), si.bits(B), "e4m3fn", scale_a=sa, scale_b=sb), "bf16")
+    Bt = B.t().contiguous()
+    dev = torch.device("cuda:0")
+    pg.pgemm_set_fp8_scales(handle, sa, sb)
+    pg.pgemm_set_b_layout(handle, pg.PGEMM_B_NK)
+    try:
+        for mode in range(5):
+            T = pg.pgemm_query_launch(handle, M, N, K, F8, mode, 0)["tiles"]
+            tr = torch.zeros(4 * T, dtype=torch.int64, device=dev)
+            pg.pgemm_set_tile_trace(handle, tr)
+            try:
+                say(f"case fp8 NK scales trace mode {mode} T={T}")
+                c = run(pg, handle, A, Bt, M, N, K, F8, mode)
+            finally:
+                pg.pgemm_set_tile_trace(handle, None)
+            assert np.array_equal(c, want), (mode, np.argwhere(c != want)[:5])
+            t = tr.view(T, 4).cpu().numpy()
+            assert (t[:, 2] > 0).all() and (t[:, 2] <= t[:, 3]).all(), mode
+    finally:
+        pg.pgemm_set_fp8_scales(handle, 1.0, 1.0)
+        pg.pgemm_set_b_layout(handle, pg.PGEMM_B_KN)
