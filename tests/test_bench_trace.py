@@ -1,4 +1,10 @@
-"""CPU check of the benchmark's tail measure on hand-made tile traces."""
+"""CPU checks of the benchmark's host logic: the tail measure on hand-made tile
+traces, the custom-workload flags, and the one-GPU rule."""
+import json
+import os
+import subprocess
+import sys
+
 import numpy as np
 
 import bench
@@ -36,3 +42,14 @@ def test_custom_workload_from_flags(monkeypatch):
     assert dtype == "bf16" and kind == "uniform"
     # the non-persistent mode ignores grid multiples; the persistent ones run each
     assert probs == [(1000, 2048, K, m, g) for K in (256, 512, 768) for m, g in ((0, 0), (1, 1), (1, 2))]
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    """The benchmark runs on one GPU; --gpus above 1 exits (status 2) with a JSON message,
+    before anything touches a device."""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], cwd=root, capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert "one GPU" in msg["error"] and msg["n_gpus_requested"] == 2
