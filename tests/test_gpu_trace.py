@@ -118,3 +118,33 @@ def test_short_trace_is_rejected_before_launch(pg, handle):
     torch.cuda.synchronize()
     assert (C.cpu() == 3.0).all()  # nothing ran
     assert (tr.cpu() == 0).all()
+
+
+def test_workgroups_dispatch_round_robin_over_xcds(pg):
+    """The XCD-aware tile order assumes workgroup w runs on XCD w mod 8 (round-robin
+    dispatch over the 8 XCDs of a whole MI355X). The trace's XCD ids pin that assumption;
+    a partitioned device (fewer CUs visible) has other rules and is skipped."""
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("not a whole 256-CU device")
+    dev = torch.device("cuda:0")
+    M = N = 8192
+    K = 256
+    A = torch.zeros(M, K, dtype=torch.float16, device=dev)
+    B = torch.zeros(K, N, dtype=torch.float16, device=dev)
+    C = torch.empty(M, N, dtype=torch.float16, device=dev)
+    h = pg.pgemm_create(0)
+    try:
+        for mode in (0, 1, 2):
+            T = pg.pgemm_query_launch(h, M, N, K, 0, mode, 0)["tiles"]
+            tr = torch.zeros(4 * T, dtype=torch.int64, device=dev)
+            pg.pgemm_set_tile_trace(h, tr)
+            try:
+                say(f"case xcd dispatch mode {mode}")
+                pg.pgemm_run(h, A, B, C, M, N, K, 0, mode, 0)
+                torch.cuda.synchronize()
+            finally:
+                pg.pgemm_set_tile_trace(h, None)
+            t = tr.view(T, 4).cpu().numpy()
+            assert np.array_equal(t[:, 1], t[:, 0] % 8), mode
+    finally:
+        pg.pgemm_destroy(h)
