@@ -174,6 +174,21 @@ int pgemm_run(pgemm_handle_t h, const void* A, const void* B, void* C, int64_t M
  * NULL is accepted (no-op). */
 int pgemm_destroy(pgemm_handle_t h);
 
+/* pgemm_run with leading dimensions, for operands that are row-major views
+ * inside larger allocations: A[i][k] at A + i*lda + k, B[k][n] at
+ * B + k*ldb + n (or, with PGEMM_B_NK, at B + n*ldb + k), C[i][j] at
+ * C + i*ldc + j, all counted in elements. pgemm_run is this call with
+ * lda = K, ldb = N (K for PGEMM_B_NK) and ldc = N. Requires ldc >= N and,
+ * when K > 0, lda >= K and ldb >= the length of B's rows (N, or K for
+ * PGEMM_B_NK); each below 2^31; else PGEMM_ERR_INVALID_ARG. Only the M x N
+ * window of C is written. The fast kernel additionally needs lda and ldb
+ * to be multiples of 16 bytes of elements and ldc a multiple of 8 (16-byte
+ * rows of C); otherwise the generic kernel runs. Leading dimensions whose
+ * tile spans exceed 32-bit buffer offsets give PGEMM_ERR_UNSUPPORTED.
+ * Everything else is as for pgemm_run. */
+int pgemm_run_ld(pgemm_handle_t h, const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+                 int64_t M, int64_t N, int64_t K, int dtype, int sched_mode, int grid_multiple);
+
 /* Watchdog wait: poll the handle's stream (hipStreamQuery, about every
  * 50 microseconds) until all work enqueued on it has finished, or until
  * timeout_ms milliseconds have passed. Returns PGEMM_OK when the stream is

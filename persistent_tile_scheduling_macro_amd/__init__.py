@@ -61,6 +61,7 @@ def _sig(name, restype, *argtypes):
 _create = _sig("pgemm_create", _int, ctypes.POINTER(_vp), _int)
 _set_stream = _sig("pgemm_set_stream", _int, _vp, _vp)
 _run = _sig("pgemm_run", _int, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int)
+_run_ld = _sig("pgemm_run_ld", _int, _vp, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _int, _int, _int)
 _destroy = _sig("pgemm_destroy", _int, _vp)
 _status_string = _sig("pgemm_status_string", ctypes.c_char_p, _int)
 _last_error = _sig("pgemm_last_error", ctypes.c_char_p, _vp)
@@ -134,6 +135,14 @@ def pgemm_run(h, A, B, C, M: int, N: int, K: int, dtype: int, sched_mode: int, g
     """Enqueue C = A @ B (device pointers or tensors) on the handle's stream."""
     _check(_run(h, _ptr(A), _ptr(B), _ptr(C), int(M), int(N), int(K), int(dtype), int(sched_mode),
                 int(grid_multiple)), h)
+
+
+def pgemm_run_ld(h, A, lda: int, B, ldb: int, C, ldc: int, M: int, N: int, K: int, dtype: int,
+                 sched_mode: int, grid_multiple: int = 0) -> None:
+    """pgemm_run with leading dimensions (in elements) for row-major views; pointers or tensors
+    (a tensor's data_ptr() is the view's first element)."""
+    _check(_run_ld(h, _ptr(A), int(lda), _ptr(B), int(ldb), _ptr(C), int(ldc), int(M), int(N), int(K),
+                   int(dtype), int(sched_mode), int(grid_multiple)), h)
 
 
 def pgemm_destroy(h) -> None:

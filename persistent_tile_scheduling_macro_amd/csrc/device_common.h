@@ -59,6 +59,7 @@ struct Params {
   const uint8_t* B;
   uint8_t* C;
   int M, N, K;
+  int lda, ldb, ldc; // leading dimensions in elements (A rows, B rows in its layout, C rows)
   int n_m, n_n, T; // tile grid and tile count
   int G;           // workgroups launched
   int group_m;     // GROUP_SIZE_M of the tile order (>= 1)

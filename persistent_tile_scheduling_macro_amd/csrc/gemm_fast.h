@@ -233,9 +233,9 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, Tile<CFG>::MIN_WAVES_PE
   // k-steps per tile, rounded up to even so that every tile starts on stage
   // 0 (an extra step reads zeros: it lies past K)
   const int nk = ((K + BK - 1) / BK + 1) & ~1;
-  const int64_t lda = (int64_t)K * ES; // bytes per row of A
-  const int64_t ldb = BT ? (int64_t)K * ES : (int64_t)N * ES; // bytes per row of B (or of N x K B)
-  const int64_t ldc = N;               // elements per row of C
+  const int64_t lda = (int64_t)p.lda * ES; // bytes per row of A
+  const int64_t ldb = (int64_t)p.ldb * ES; // bytes per row of B (K x N, or N x K when BT)
+  const int64_t ldc = p.ldc;               // elements per row of C
 
   // ---- per-lane constants of the global -> LDS copy ------------------------
   // Instruction q = wave + WAVES*j fills one 1 KiB block of a stage: A rows
@@ -740,7 +740,7 @@ __global__ void __launch_bounds__(256) sk_fixup_kernel(Params p) {
       lo *= p.c_scale;
       hi *= p.c_scale;
     }
-    store8(reinterpret_cast<out_t*>(p.C) + (int64_t)m * p.N + n, lo, hi, false);
+    store8(reinterpret_cast<out_t*>(p.C) + (int64_t)m * p.ldc + n, lo, hi, false);
   }
   if (blockIdx.y == 0 && threadIdx.x == 0) {
     if (p.visits) atomicAdd(p.visits + tile, 1);

@@ -64,13 +64,13 @@ __global__ void __launch_bounds__(THREADS) gemm_generic_kernel(Params p) {
       for (int e = tid; e < BM * KG; e += THREADS) {
         const int r = e / KG, k = e % KG;
         const int gm = m0 + r, gk = k0 + k;
-        elem_t v = (gm < p.M && gk < p.K) ? A[(int64_t)gm * p.K + gk] : (elem_t)0;
+        elem_t v = (gm < p.M && gk < p.K) ? A[(int64_t)gm * p.lda + gk] : (elem_t)0;
         *reinterpret_cast<elem_t*>(sA + r * ROWB + k * ES) = v;
       }
       for (int e = tid; e < BN * KG; e += THREADS) {
         const int k = e / BN, c = e % BN;
         const int gk = k0 + k, gn = n0 + c;
-        elem_t v = (gk < p.K && gn < p.N) ? B[p.b_nk ? (int64_t)gn * p.K + gk : (int64_t)gk * p.N + gn] : (elem_t)0;
+        elem_t v = (gk < p.K && gn < p.N) ? B[p.b_nk ? (int64_t)gn * p.ldb + gk : (int64_t)gk * p.ldb + gn] : (elem_t)0;
         *reinterpret_cast<elem_t*>(sB + c * ROWB + k * ES) = v;
       }
       __syncthreads();
@@ -106,7 +106,7 @@ __global__ void __launch_bounds__(THREADS) gemm_generic_kernel(Params p) {
         const int n = n0 + wn * 32 + j * 16 + 4 * g;
         for (int e = 0; e < 4; ++e)
           if (n + e < p.N)
-            C[(int64_t)m * p.N + n + e] = to_out(ES == 1 ? acc[i][j][e] * p.c_scale : acc[i][j][e], (out_t*)nullptr);
+            C[(int64_t)m * p.ldc + n + e] = to_out(ES == 1 ? acc[i][j][e] * p.c_scale : acc[i][j][e], (out_t*)nullptr);
       }
     }
     if (tid == 0) {
@@ -129,11 +129,12 @@ __global__ void __launch_bounds__(THREADS) gemm_generic_kernel(Params p) {
   }
 }
 
-// C = 0 for K = 0 (an empty sum), M x N outputs.
+// C = 0 for K = 0 (an empty sum): rows x cols outputs, rows ldc elements apart.
 template <class OutT>
-__global__ void fill_zero_kernel(OutT* C, int64_t n) {
+__global__ void fill_zero_kernel(OutT* C, int64_t rows, int64_t cols, int64_t ldc) {
+  const int64_t n = rows * cols;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-    C[i] = (OutT)0.0f;
+    C[(i / cols) * ldc + i % cols] = (OutT)0.0f;
 }
 
 } // namespace generic

@@ -23,8 +23,8 @@ kernel_fn pick_fixup_f16(int body);
 kernel_fn pick_fixup_bf16(int body);
 kernel_fn pick_fixup_f8(int body);
 
-// K == 0: C = 0 (an empty sum). n = M * N output elements.
-void launch_fill_zero(void* C, int64_t n, hipStream_t stream);
+// K == 0: C = 0 (an empty sum), rows x cols elements with rows ldc elements apart.
+void launch_fill_zero(void* C, int64_t rows, int64_t cols, int64_t ldc, hipStream_t stream);
 
 // Benchmark aid (hold.hip): n workgroups that each hold a whole CU's LDS
 // until the constant-rate clock has advanced by `ticks`.

@@ -264,22 +264,42 @@ int pgemm_set_stream(pgemm_handle_t h, void* hip_stream) {
 
 int pgemm_run(pgemm_handle_t h, const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
               int dtype, int sched_mode, int grid_multiple) {
+  if (!h) return PGEMM_ERR_INVALID_ARG;
+  return pgemm_run_ld(h, A, K, B, h->b_nk ? K : N, C, N, M, N, K, dtype, sched_mode, grid_multiple);
+}
+
+int pgemm_run_ld(pgemm_handle_t h, const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+                 int64_t M, int64_t N, int64_t K, int dtype, int sched_mode, int grid_multiple) {
   int rc = check_common(h, M, N, K, dtype, sched_mode);
   if (rc != PGEMM_OK) return rc;
   h->last_error[0] = 0;
   if (M == 0 || N == 0) return PGEMM_OK;
   if (!C) return fail(h, PGEMM_ERR_INVALID_ARG, "C is NULL");
+  // a leading dimension covers its row and stays below 2^31 elements
+  const int64_t brow = h->b_nk ? K : N;
+  if (ldc < N || (K > 0 && (lda < K || ldb < brow)) || lda > INT32_MAX || ldb > INT32_MAX || ldc > INT32_MAX)
+    return fail(h, PGEMM_ERR_INVALID_ARG, "leading dimensions lda=%lld ldb=%lld ldc=%lld too small or too large",
+                (long long)lda, (long long)ldb, (long long)ldc);
   if (hipSetDevice(h->device) != hipSuccess) return fail(h, PGEMM_ERR_HIP, "hipSetDevice failed");
   if (K == 0) {
-    launch_fill_zero(C, M * N, h->stream);
+    launch_fill_zero(C, M, N, ldc, h->stream);
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? PGEMM_OK : fail(h, PGEMM_ERR_HIP, "zero-fill launch: %s", hipGetErrorString(e));
   }
   if (!A || !B) return fail(h, PGEMM_ERR_INVALID_ARG, "A or B is NULL");
-  const bool fast = sizes_fast(dtype, N, K) && ptrs_fast(A, B, C);
+  const int64_t per16 = 16 / esize_of(dtype); // elements per 16 bytes
+  const bool fast = sizes_fast(dtype, N, K) && ptrs_fast(A, B, C) && lda % per16 == 0 && ldb % per16 == 0 &&
+                    ldc % 8 == 0;
   Plan pl;
   rc = plan_launch(h, M, N, K, dtype, sched_mode, grid_multiple, fast, &pl);
   if (rc != PGEMM_OK) return rc;
+  if (fast) {
+    // per-tile A (and N x K B) offsets reach BM (BN) rows; per-step K x N B offsets reach BK rows
+    const int64_t es = esize_of(dtype), lim = (int64_t)1 << 31;
+    const int64_t b_span = h->b_nk ? (int64_t)pl.bn * ldb * es : (int64_t)pl.bk * ldb * es;
+    if ((int64_t)pl.bm * lda * es >= lim || b_span >= lim)
+      return fail(h, PGEMM_ERR_UNSUPPORTED, "leading dimensions too long for 32-bit buffer offsets");
+  }
   if (h->visits && pl.T > h->n_visits)
     return fail(h, PGEMM_ERR_INVALID_ARG, "tile counter holds %lld entries, run has %lld tiles",
                 (long long)h->n_visits, (long long)pl.T);
@@ -296,6 +316,9 @@ int pgemm_run(pgemm_handle_t h, const void* A, const void* B, void* C, int64_t M
   p.M = (int)M;
   p.N = (int)N;
   p.K = (int)K;
+  p.lda = (int)lda;
+  p.ldb = (int)ldb;
+  p.ldc = (int)ldc;
   p.n_m = (int)pl.n_m;
   p.n_n = (int)pl.n_n;
   p.T = (int)pl.T;
