@@ -475,7 +475,10 @@ def tile_trace_summary(pg, h, probs, operands, outs, dt_code, torch, np, raw_pat
             "busy_frac": round(busy / (slots * (t1 - t0)), 4) if t1 > t0 else None,
             "drain_us": round((t1 - drain_from) * us, 1),
             "tile_us_median": round(float(np.median(en - st)) * us, 1),
-            "xcd_is_wg_mod_8": round(float((xcd[own] == wg[own] % 8).mean()), 4) if own.any() else None,
+            # workgroups are dealt round-robin over the 8 XCDs from a starting XCD that carries over
+            # between launches: the fraction of tiles on XCD (w + r) mod 8 for the launch's rotation r
+            "xcd_round_robin": (round(float(np.bincount((xcd[own] - wg[own]) % 8, minlength=8).max() / own.sum()), 4)
+                                if own.any() else None),
         }
     if raw_path:
         np.savez(raw_path, **raw)

@@ -82,12 +82,13 @@ struct Params {
 // Tile id t -> (pid_m, pid_n). Two steps, applied identically in every
 // scheduling mode so that only the scheduling differs between modes:
 //
-// 1. XCD-aware remap. Workgroup ids are dispatched round-robin over the 8
-//    XCDs, and in the persistent modes workgroup w owns tiles t = w (mod G)
-//    with G a multiple of the CU count, so t mod 8 names the XCD that runs
-//    t. Inside each full chunk of `xcd_chunk` tiles the remap makes each
-//    XCD's tiles consecutive, so step 2 gives every XCD a compact block of
-//    the output (shared operand rows and columns stay in that XCD's L2).
+// 1. XCD-aware remap. Workgroup ids are dealt round-robin over the 8 XCDs
+//    (from a starting XCD that carries over between launches), and in the
+//    persistent modes workgroup w owns tiles t = w (mod G) with G a multiple
+//    of the CU count, so all tiles with the same t mod 8 run on one XCD.
+//    Inside each full chunk of `xcd_chunk` tiles the remap makes each such
+//    class consecutive, so step 2 gives every XCD a compact block of the
+//    output (shared operand rows and columns stay in that XCD's L2).
 // 2. Grouped order (the GROUP_SIZE_M knob of the Triton persistent-matmul
 //    issue, "What I've tried" / follow-up comment): walk down groups of
 //    group_m tile rows column by column. group_m = 1 is plain row-major.
@@ -135,13 +136,20 @@ __host__ __device__ inline void tile_coords(int t, const Params& p, int* pm, int
 // treated as a failed claim, so a corrupted counter never names a tile
 // outside the grid. (Claims are handed out in the order they arrive, which
 // at a launch's start is close to workgroup order, so the tiles a
-// workgroup gets are close to the ones the static mode would give it and
-// stay on the same XCD: workgroup w runs on XCD w % 8. Separate per-XCD
-// counters measured slower.) Host-callable too, so a CPU test can race it.
-__host__ __device__ inline int claim_tile(int* counter, int T, int offset, int total) {
-  const int c = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// workgroup gets are close to the ones the static mode would give it.
+// Separate per-XCD counters measured slower.) Host-callable too, so a CPU test can race it.
+__host__ __device__ inline int claim_raw(int* counter) {
+  return __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// The rest of a claim once its counter value c is back: the last claim of the launch resets
+// the counter; c names tile c + offset, or none (T). Split from claim_raw so that a kernel
+// can issue the atomic and finish the claim later, when the value has returned.
+__host__ __device__ inline int claim_finish(int* counter, int c, int T, int offset, int total) {
   if (c == total - 1) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return (c < 0 || c >= total || c + offset >= T) ? T : c + offset;
+}
+__host__ __device__ inline int claim_tile(int* counter, int T, int offset, int total) {
+  return claim_finish(counter, claim_raw(counter), T, offset, total);
 }
 
 // Claim parameters of a scheduling mode: (offset, total) of claim_tile.

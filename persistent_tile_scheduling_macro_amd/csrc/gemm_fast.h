@@ -320,6 +320,14 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, Tile<CFG>::MIN_WAVES_PE
   // work units come from the walkers below.)
   constexpr bool CLAIMS = SCHED == kDynamic || SCHED == kCancel;
   bool claim_live = false;    // thread 0 only: the last claim got a tile
+  // Cancel-and-reuse with tiles of >= 4 k-steps: the claim of tile sequence number 1 is
+  // issued after the first k-step's barrier and finished at the second's, not in the
+  // prologue. Made in the prologue, the claims of the first workgroups to start took tiles
+  // before the last workgroups of the same wave had made their first claim (measured at
+  // 4096^3, 256 tiles on 256 workgroups: 16 workgroups ran two tiles and 16 none, doubling
+  // the run). The producer needs tile 1 only from step nk - 2 >= 2 on.
+  const bool defer_t1 = SCHED == kCancel && nk >= 4;
+  int t1_raw = 0; // thread 0: the deferred claim's counter value
   auto tile_of = [&](int q) __attribute__((always_inline)) -> int {
     if constexpr (SCHED == kNonPersistent) {
       return q == 0 ? (int)blockIdx.x : T;
@@ -566,7 +574,17 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, Tile<CFG>::MIN_WAVES_PE
     const uint8_t* sA = bufA(cst);
     const uint8_t* sB = bufB(cst);
     wait_vmcnt<0>();
+    if constexpr (SCHED == kCancel) {
+      if (defer_t1 && cs == 1 && tid == 0) { // the deferred claim has returned: publish it
+        const int t1 = claim_finish(p.counter, t1_raw, T, claim_offset<SCHED>(G), claim_total<SCHED>(T, G));
+        s_ring[1] = t1;
+        claim_live = t1 < T;
+      }
+    }
     __syncthreads();
+    if constexpr (SCHED == kCancel) {
+      if (defer_t1 && cs == 0 && tid == 0) t1_raw = claim_raw(p.counter);
+    }
     begin_copy();
     has_next = p_busy;
 #pragma unroll
@@ -602,7 +620,17 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, Tile<CFG>::MIN_WAVES_PE
     has_next = issued > cs + 1;
     if (has_next) {
       wait_vmcnt<0>(); // this wave's copy of step cs+1 (and any older stores) landed
+      if constexpr (SCHED == kCancel) {
+        if (defer_t1 && cs == 1 && tid == 0) { // the deferred claim has returned: publish it
+          const int t1 = claim_finish(p.counter, t1_raw, T, claim_offset<SCHED>(G), claim_total<SCHED>(T, G));
+          s_ring[1] = t1;
+          claim_live = t1 < T;
+        }
+      }
       __syncthreads(); // every wave's; and every wave has read all of stage C
+      if constexpr (SCHED == kCancel) {
+        if (defer_t1 && cs == 0 && tid == 0) t1_raw = claim_raw(p.counter);
+      }
       begin_copy();    // step cs + 2 into stage C
       static_for<L / 2>([&](auto pc) __attribute__((always_inline)) { copy_pair(cst, pc); });
     }
@@ -634,9 +662,11 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, Tile<CFG>::MIN_WAVES_PE
       // dynamic with G >= T: no tile lies beyond the grid's own, so no claim is made at all
       // (the counter is left at 0); cancel-and-reuse always claims
       const bool may_claim = SCHED == kCancel || G < T;
-      const int t1 = (t0 < T && may_claim) ? claim_tile(p.counter, T, claim_offset<SCHED>(G), claim_total<SCHED>(T, G)) : T;
-      s_ring[1] = t1;
-      claim_live = t1 < T;
+      if (!defer_t1) {
+        const int t1 = (t0 < T && may_claim) ? claim_tile(p.counter, T, claim_offset<SCHED>(G), claim_total<SCHED>(T, G)) : T;
+        s_ring[1] = t1;
+        claim_live = t1 < T;
+      }
     }
     __syncthreads();
     if constexpr (SCHED == kCancel) {
