@@ -109,6 +109,9 @@ def parse():
                          "nk = N x K row-major (B transposed, as a linear layer stores its weight)")
     ap.add_argument("--tile", default="auto", choices=["auto", "256", "128"],
                     help="macro tile of the fast kernel (auto: the library's default choice)")
+    ap.add_argument("--vendor", action="store_true",
+                    help="also time torch's own GEMM (hipBLASLt) on the same operands, interleaved with "
+                         "pgemm's static mode in the same process (context, not the metric)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (reference for rocprof HBM counters)")
     return ap.parse_args()
@@ -379,6 +382,10 @@ def main():
         ps = [p for p in probs if p[3] == mode]
         mode_tflops[MODE_NAMES[mode]] = round(sum(flops[p] for p in ps) / sum(float(np.median(per[p])) for p in ps) / 1e12, 1)
 
+    vendor_info = None
+    if args.vendor:
+        vendor_info = vendor_leg(pg, h, probs, operands, outs, dtype, dt_code, args.b_layout, stream, torch, np)
+
     trace_info = None
     if args.trace:
         trace_info = tile_trace_summary(pg, h, probs, operands, outs, dt_code, torch, np, args.trace_out)
@@ -412,10 +419,58 @@ def main():
         result["graph"] = graph_info
     if trace_info:
         result["tile_trace"] = trace_info
+    if vendor_info:
+        result["vendor"] = vendor_info
     if args.table:
         with open(args.table, "w") as f:
             json.dump({"result": result, "table": table}, f, indent=1)
     print(json.dumps(result), flush=True)
+
+
+def vendor_leg(pg, h, probs, operands, outs, dtype, dt_code, b_layout, stream, torch, np, rounds=4, reps=5):
+    """torch's own GEMM on the workload's operands, beside pgemm's static mode.
+
+    Per distinct (M, N, K): `rounds` alternations of `reps` back-to-back vendor launches and
+    `reps` pgemm static launches, one event pair around each group (same stream), so both
+    see the same clock and power state. fp16/bf16 use torch.matmul with B as stored (K x N,
+    or the transpose of an N x K B). fp8 uses torch._scaled_mm, which takes B column-major
+    (K-contiguous): that is the stored N x K B, or an N x K copy made here for a K x N one.
+    Returns total TFLOP/s of each side over the distinct shapes (sum of flops over sum of
+    median times) and their ratio."""
+    one = torch.ones((), dtype=torch.float32, device=outs[next(iter(outs))].device)
+    t_v, t_p, fl = 0.0, 0.0, 0.0
+    for (m, n, K) in sorted({p[:3] for p in probs}):
+        A, B = operands[(m, n, K)]
+        C = outs[(m, n)]
+        if dtype == "e4m3fn":
+            Bnk = B if b_layout == "nk" else B.t().contiguous()
+            def vendor():
+                torch._scaled_mm(A, Bnk.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+        else:
+            Bkn = B.t() if b_layout == "nk" else B
+            def vendor():
+                torch.matmul(A, Bkn, out=C)
+        def ours():
+            pg.pgemm_run(h, A, B, C, m, n, K, dt_code, 1, 0)
+        tv, tp = [], []
+        for fn in (vendor, ours):  # untimed first calls (library heuristics, kernel loads)
+            fn()
+        for _ in range(rounds):
+            for fn, acc in ((vendor, tv), (ours, tp)):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(reps):
+                    fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                acc.append(e0.elapsed_time(e1) * 1e-3 / reps)
+        t_v += float(np.median(tv))
+        t_p += float(np.median(tp))
+        fl += 2.0 * m * n * K
+    lib = "torch._scaled_mm (B column-major)" if dtype == "e4m3fn" else "torch.matmul"
+    return {"library": lib, "tflops": round(fl / t_v / 1e12, 1), "pgemm_static_tflops": round(fl / t_p / 1e12, 1),
+            "pgemm_over_vendor": round(t_v / t_p, 3),
+            "timing": f"{rounds} alternations of {reps} launches per side and shape, events on one stream"}
 
 
 def drain_start(st, en, slots, np):

@@ -53,3 +53,11 @@ def test_more_than_one_gpu_is_refused_with_a_message():
     assert r.returncode == 2
     msg = json.loads(r.stdout.strip().splitlines()[-1])
     assert "one GPU" in msg["error"] and msg["n_gpus_requested"] == 2
+
+
+def test_vendor_flag_parses(monkeypatch):
+    monkeypatch.setattr("sys.argv", ["bench.py", "--workload", "fp8", "--b-layout", "nk", "--vendor"])
+    args = bench.parse()
+    assert args.vendor and args.b_layout == "nk"
+    monkeypatch.setattr("sys.argv", ["bench.py"])
+    assert not bench.parse().vendor
