@@ -567,7 +567,9 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, Tile<CFG>::MIN_WAVES_PE
   // ---- one k-step on stage C --------------------------------------------------
   int cs = 0; // consumer step
   bool has_next = true;
-  // fp8 step: barrier at the top, next copy right after it.
+  // fp8 step: barrier at the top, next copy right after it. The B fragments
+  // and A's first row block are read before the first MFMA row; each further
+  // A row block is read one MFMA row ahead (a burst of all reads was slower).
   auto step_top = [&](auto cst) __attribute__((always_inline)) {
     constexpr int C = decltype(cst)::value;
     typedef std::integral_constant<int, C ^ 1> ICN;
@@ -589,10 +591,10 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, Tile<CFG>::MIN_WAVES_PE
     has_next = p_busy;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) read_b_frag(I0{}, sB, 0, nb);
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) read_a_frag(I0{}, sA, 0, mb);
+    read_a_frag(I0{}, sA, 0, 0);
     static_for<MB>([&](auto mbc) __attribute__((always_inline)) {
       constexpr int MBI = decltype(mbc)::value;
+      if constexpr (MBI + 1 < MB) read_a_frag(I0{}, sA, 0, MBI + 1); // one row ahead
       mfma_row(I0{}, MBI);
       if constexpr (MBI < L / 2) copy_pair(ICN{}, std::integral_constant<int, MBI>{});
       __builtin_amdgcn_sched_barrier(0);
