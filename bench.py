@@ -3,17 +3,27 @@
 
 Metric: GEMM TFLOPS (2*M*N*K / time) and its fraction of the dense MFMA
 peak, swept over K, with the non-persistent, static-persistent and
-dynamic-persistent modes side by side (the sweep of the Triton
-persistent-matmul issue, "Describe the issue": M = N = 4096, K from 128
-to 4096 in steps of 128, fp16).
+dynamic-persistent modes side by side (the sweeps of the Triton
+persistent-matmul issue, "Describe the issue": M = N = 8192, K from 256
+to 8192 in steps of 256 -- the default workload, whose last point is the
+8192^3 target -- and M = N = 4096, K from 128 to 4096 in steps of 128).
 
 One "step" is one pass of the whole workload: every K of the sweep in
-every scheduling mode, inputs already resident in device memory.
+every scheduling mode and grid multiple, inputs already resident in
+device memory.
 `value` is the step's total algorithmic flops over its total time, from
 K steps launched back to back with nothing between the launches. The
 per-(K, mode) table and the roofline's launch durations come from a
 second pass of the same K steps with HIP events around every launch
 (those events add gaps, so they stay out of the timed region).
+
+After the timed workload the default run also measures, in the same
+process and outside the timed region: a small-K pass (100 launches per
+(K, mode) point, the mode order rotating from launch to launch, for the
+persistent-vs-non-persistent crossover), and a summary of the other
+configured workloads (fp16 256^3, the 4096^2 sweep at both macro tiles,
+fp8 8192^3, the bf16 tail set), each mode's TFLOP/s and fraction of the
+dtype's dense peak.
 
 Prints ONE JSON line on stdout; the per-(K, mode) table goes to
 --table (JSON) when given.
@@ -36,6 +46,8 @@ MODE_NAMES = {0: "nonpersistent", 1: "static", 2: "dynamic", 3: "cancel", 4: "st
 
 WORKLOADS = {
     # name: (description, dtype, M, N, K list, modes, grid multiples, input kind, workload id)
+    "small256": ("fp16 GEMM M=N=K=256, uniform[-1,1], fp16 C; non-persistent, static and dynamic (one tile)",
+                 "f16", 256, 256, [256], [0, 1, 2], [0], "uniform", 1),
     "sweep4k": ("fp16 GEMM M=N=4096, K=128..4096 step 128, uniform[-1,1], fp32 accumulate, fp16 C; "
                 "non-persistent, static and dynamic persistent per K", "f16", 4096, 4096,
                 list(range(128, 4097, 128)), [0, 1, 2], [0], "uniform", 2),
@@ -76,7 +88,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="sweep4k", choices=sorted(WORKLOADS) + ["custom"],
+    ap.add_argument("--workload", default="sweep8k", choices=sorted(WORKLOADS) + ["custom"],
                     help="a configured workload, or 'custom' built from --prec/--M/--N/--K-range/--K-step")
     ap.add_argument("--prec", default="fp16", choices=["fp16", "bf16", "fp8"],
                     help="custom workload: input precision (fp8 = OCP e4m3, bf16 output)")
@@ -93,7 +105,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample duration")
     ap.add_argument("--modes", default=None, help="comma-separated subset of scheduling modes (0..4)")
     ap.add_argument("--no-small-k-latency", action="store_true",
-                    help="skip the 100-launch latency pass for K <= 512 (profiled runs: one launch per point)")
+                    help="skip the 100-launch small-K crossover pass (profiled runs: one launch per point)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured once as a HIP graph and replayed (launch overhead removed)")
     ap.add_argument("--hold-cus", type=int, default=64, help="uneven workload: CUs held by the co-running kernel")
@@ -109,6 +121,17 @@ def parse():
                          "nk = N x K row-major (B transposed, as a linear layer stores its weight)")
     ap.add_argument("--tile", default="auto", choices=["auto", "256", "128"],
                     help="macro tile of the fast kernel (auto: the library's default choice)")
+    ap.add_argument("--mainloop", default="auto", choices=["auto", "lockstep", "pingpong"],
+                    help="wave schedule of the 256 x 256 tile (auto: the library's default choice)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the summary of the other configured workloads after the timed one")
+    ap.add_argument("--small-k-max", type=int, default=None,
+                    help="largest K of the small-K crossover pass (default: 2048 for sweep8k, 1024 for sweep4k, "
+                         "512 otherwise)")
+    ap.add_argument("--oracle-timing", action="store_true",
+                    help="only time the CPU oracle in full on every configured problem it can finish in minutes "
+                         "(256^3; 8192^3 fp8; the bf16 tail set; 4096^2 at K = 128, 1024, 4096; 8192^2 at "
+                         "K = 256, 2048, 8192) and print one JSON line")
     ap.add_argument("--vendor", action="store_true",
                     help="also time torch's own GEMM (hipBLASLt) on the same operands, interleaved with "
                          "pgemm's static mode in the same process (context, not the metric)")
@@ -118,7 +141,7 @@ def parse():
 
 
 CSRC = os.path.join(ROOT, "persistent_tile_scheduling_macro_amd", "csrc")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_gemm_fast_f16_sweep4k.txt")
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def source_digest() -> str:
@@ -140,24 +163,30 @@ def source_digest() -> str:
 
 
 def measured_traffic(kernel: str, workload: str):
-    """Calibrated HBM bytes per launch of `kernel` from the committed rocprofv3
-    summary (one key line per kernel of the workload), or None if there is none
-    or the kernel source changed since."""
-    try:
+    """Calibrated HBM bytes per launch of `kernel` from a committed rocprofv3
+    summary (profiles/hbm_traffic_*.txt: one key line per kernel of the
+    workload), or None if there is none for this workload or the kernel
+    source changed since."""
+    import glob
+
+    digest = source_digest()
+    for path in sorted(glob.glob(os.path.join(PROFILES, "hbm_traffic_*.txt"))):
         kv = {}
-        with open(TRAFFIC_FILE) as f:
-            for line in f:
-                if ":" in line and not line.startswith("#"):
-                    k, v = line.split(":", 1)
-                    kv[k.strip()] = v.strip()
-    except OSError:
-        return None
-    if kv.get("source_sha256") != source_digest() or kv.get("workload") != workload:
-        return None
-    try:
-        return float(kv[f"hbm_bytes_per_launch {kernel}"])
-    except (KeyError, ValueError):
-        return None
+        try:
+            with open(path) as f:
+                for line in f:
+                    if ":" in line and not line.startswith(("#", " ")):
+                        k, v = line.split(":", 1)
+                        kv[k.strip()] = v.strip()
+        except OSError:
+            continue
+        if kv.get("workload") != workload or kv.get("source_sha256") != digest:
+            continue
+        try:
+            return float(kv[f"hbm_bytes_per_launch {kernel}"])
+        except (KeyError, ValueError):
+            return None
+    return None
 
 
 def copy_calibration(mib: int) -> None:
@@ -187,36 +216,32 @@ def problems(wl):
     return desc, dtype, kind, wid, out
 
 
-def main():
-    args = parse()
-    if args.copy_calibration:
-        copy_calibration(args.copy_calibration)
-        return
-    if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1",
-                          "n_gpus_requested": args.gpus}))
-        sys.exit(2)
-    import numpy as np
-    import torch
+SCHED_NAMES = {0: "kNonPersistent", 1: "kStatic", 2: "kDynamic", 3: "kCancel", 4: "kStreamK"}
+DT_NAMES = {"f16": "kF16", "bf16": "kBF16", "e4m3fn": "kF8E4M3"}
 
-    import persistent_tile_scheduling_macro_amd as pg
-    import seeded_inputs as si
 
-    if not torch.cuda.is_available():
-        print(json.dumps({"error": "no GPU visible"}))
-        sys.exit(1)
-    dev = torch.device("cuda:0")
-    if args.workload == "uneven":
-        return run_uneven(args, pg, si, torch, np)
-    if args.workload == "custom":
-        add_custom_workload(args)
-    desc, dtype, kind, wid, probs = problems(args.workload)
-    if args.modes:
+def kernel_name(dtype, mode, info):
+    """Name of the kernel that computes a launch's whole tiles (the key of the traffic profiles)."""
+    if not info["fast_path"]:
+        return f"gemm_generic_kernel<{DT_NAMES[dtype]}, {SCHED_NAMES[mode]}>"
+    if info.get("body") == 2:  # ping-pong; stream-K's whole waves run in its static kernel
+        return f"gemm_pp_kernel<{DT_NAMES[dtype]}, {SCHED_NAMES[1 if mode == 4 else mode]}>"
+    return f"gemm_fast_kernel<{DT_NAMES[dtype]}, {SCHED_NAMES[mode]}, kTile{info['bm']}>"
+
+
+def variant_name(p):
+    return MODE_NAMES[p[3]] + (f"@g{p[4]}" if p[4] else "")
+
+
+def setup(pg, torch, si, args, workload, tile=None):
+    """Operands, outputs, a handle and a launch function for a configured workload."""
+    desc, dtype, kind, wid, probs = problems(workload)
+    if args.modes and workload == args.workload:
         keep = {int(x) for x in args.modes.split(",")}
         probs = [p for p in probs if p[3] in keep]
+    dev = torch.device("cuda:0")
     dt_code = {"f16": pg.PGEMM_F16, "bf16": pg.PGEMM_BF16, "e4m3fn": pg.PGEMM_F8E4M3_BF16}[dtype]
     out_dtype = torch.bfloat16 if dtype in ("bf16", "e4m3fn") else torch.float16
-
     # Inputs: drawn once at the largest shape, sliced per K (leading columns of A, rows of B).
     shapes = {}
     for (m, n, K, _, _) in probs:
@@ -228,22 +253,185 @@ def main():
         Ad, Bd = A.to(dev), B.to(dev)
         for K in set(ks):
             Bk = Bd[:K, :]
-            operands[(m, n, K)] = (Ad[:, :K].contiguous(), Bk.t().contiguous() if args.b_layout == "nk" else Bk.contiguous())
-        del A, B
+            operands[(m, n, K)] = (Ad[:, :K].contiguous(),
+                                   Bk.t().contiguous() if args.b_layout == "nk" else Bk.contiguous())
+        del A, B, Ad, Bd
     outs = {(m, n): torch.empty((m, n), dtype=out_dtype, device=dev) for (m, n) in shapes}
     torch.cuda.synchronize()
-
     stream = torch.cuda.current_stream(dev)
     h = pg.pgemm_create(0)
     pg.pgemm_set_stream(h, stream)
+    tile = tile or args.tile
     pg.pgemm_set_tile_config(h, {"auto": pg.PGEMM_TILE_AUTO, "256": pg.PGEMM_TILE_256,
-                                 "128": pg.PGEMM_TILE_128}[args.tile])
+                                 "128": pg.PGEMM_TILE_128}[tile])
+    pg.pgemm_set_mainloop(h, {"auto": pg.PGEMM_MAINLOOP_AUTO, "lockstep": pg.PGEMM_MAINLOOP_LOCKSTEP,
+                              "pingpong": pg.PGEMM_MAINLOOP_PINGPONG}[args.mainloop])
     pg.pgemm_set_b_layout(h, pg.PGEMM_B_NK if args.b_layout == "nk" else pg.PGEMM_B_KN)
 
     def launch(p):
         m, n, K, mode, gm = p
         A, B = operands[(m, n, K)]
         pg.pgemm_run(h, A, B, outs[(m, n)], m, n, K, dt_code, mode, gm)
+
+    return dict(desc=desc, dtype=dtype, kind=kind, wid=wid, probs=probs, dt_code=dt_code, operands=operands,
+                outs=outs, stream=stream, h=h, launch=launch)
+
+
+def rotated_launch_times(torch, stream, probs, launch, rounds):
+    """`rounds` rounds; each launches every problem once, with an event pair around each
+    launch, in an order rotated by one from round to round (so no variant always runs
+    first or last in a burst while the clock settles). Returns {problem: [seconds]}."""
+    n = len(probs)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+          for _ in range(rounds)]
+    order = []
+    for r in range(rounds):
+        idx = [(i + r) % n for i in range(n)]
+        order.append(idx)
+        for i in idx:
+            ev[r][i][0].record(stream)
+            launch(probs[i])
+            ev[r][i][1].record(stream)
+    torch.cuda.synchronize()
+    out = {p: [] for p in probs}
+    for r in range(rounds):
+        for i in order[r]:
+            out[probs[i]].append(ev[r][i][0].elapsed_time(ev[r][i][1]) * 1e-3)
+    return out
+
+
+def small_k_crossover(torch, np, env, k_max, rounds=100):
+    """Persistent vs non-persistent at small K: every (K, mode, grid multiple) point with
+    K <= k_max launched `rounds` times, the order rotating from round to round. Per K:
+    median, min and max per variant, the fastest variant by median, and whether the
+    non-persistent mode's median beats every persistent variant's."""
+    probs = [p for p in env["probs"] if p[2] <= k_max]
+    if not probs:
+        return None
+    for p in probs:  # warm every variant once
+        env["launch"](p)
+    torch.cuda.synchronize()
+    times = rotated_launch_times(torch, env["stream"], probs, env["launch"], rounds)
+    by_k = {}
+    for p in probs:
+        us = sorted(t * 1e6 for t in times[p])
+        by_k.setdefault(p[2], {})[variant_name(p)] = {
+            "median_us": round(float(np.median(us)), 2), "min_us": round(us[0], 2), "max_us": round(us[-1], 2),
+            "tflops_median": round(2.0 * p[0] * p[1] * p[2] / (np.median(us) * 1e-6) / 1e12, 1)}
+    points, ahead = {}, []
+    for K in sorted(by_k):
+        v = by_k[K]
+        fastest = min(v, key=lambda k: v[k]["median_us"])
+        pers = {k: x for k, x in v.items() if not k.startswith("nonpersistent")}
+        entry = {"variants": v, "fastest": fastest}
+        if "nonpersistent" in v and pers:
+            best_p = min(pers, key=lambda k: pers[k]["median_us"])
+            np_med, p_med = v["nonpersistent"]["median_us"], pers[best_p]["median_us"]
+            entry["best_persistent"] = best_p
+            entry["nonpersistent_over_best_persistent"] = round(np_med / p_med, 4)
+            # the medians' order is settled only when the two ranges [min, max] do not overlap
+            entry["separated"] = bool(v["nonpersistent"]["min_us"] > pers[best_p]["max_us"]
+                                      or pers[best_p]["min_us"] > v["nonpersistent"]["max_us"])
+            ahead.append((K, np_med <= p_med))
+        points[f"K={K}"] = entry
+    # crossover: the smallest K from which the non-persistent median is at least as fast as the
+    # best persistent one at every larger measured K (None: persistent leads at the largest K)
+    cross = None
+    for K, np_wins in reversed(ahead):
+        if not np_wins:
+            break
+        cross = K
+    return {"launches_per_point": rounds, "order": "rotated by one variant per round", "points": points,
+            "persistent_ahead_at_K": [K for K, w in ahead if not w],
+            "nonpersistent_ahead_at_K": [K for K, w in ahead if w],
+            "crossover_K": cross}
+
+
+def summarize(env, times, np, peak):
+    """Per-(K, mode) table, per-mode totals and the best variant per problem."""
+    table, mode_tflops = [], {}
+    for p in env["probs"]:
+        m, n, K, mode, gm = p
+        t = float(np.median(times[p]))
+        fl = 2.0 * m * n * K
+        byts = ESIZE[env["dtype"]] * (m * K + K * n) + 2 * m * n
+        table.append({"M": m, "N": n, "K": K, "mode": MODE_NAMES[mode], "grid_multiple": gm,
+                      "us": round(t * 1e6, 2), "tflops": round(fl / t / 1e12, 1),
+                      "frac_peak": round(fl / t / 1e12 / peak, 4),
+                      "frac_roofline": round(fl / t / 1e12 / min(peak, fl / byts * HBM_GBS / 1e3), 4)})
+    for name in sorted({variant_name(p) for p in env["probs"]}):
+        ps = [p for p in env["probs"] if variant_name(p) == name]
+        fl = sum(2.0 * p[0] * p[1] * p[2] for p in ps)
+        tt = sum(float(np.median(times[p])) for p in ps)
+        mode_tflops[name] = {"tflops": round(fl / tt / 1e12, 1), "frac_peak": round(fl / tt / 1e12 / peak, 4)}
+    return table, mode_tflops
+
+
+def config_summary(pg, torch, np, si, args):
+    """The other configured workloads, measured after the timed one with the same
+    library defaults: each (problem, mode) launched in rotated order, a few rounds."""
+    out = {}
+    plan = [("small256", "auto", 20), ("sweep4k", "auto", 5), ("sweep4k", "128", 5), ("fp8", "auto", 8),
+            ("tail", "auto", 6)]
+    for wl, tile, rounds in plan:
+        env = setup(pg, torch, si, args, wl, tile=tile)
+        try:
+            for p in env["probs"]:
+                env["launch"](p)
+            torch.cuda.synchronize()
+            times = rotated_launch_times(torch, env["stream"], env["probs"], env["launch"], rounds)
+            peak = PEAK_TFLOPS[env["dtype"]]
+            table, modes = summarize(env, times, np, peak)
+            key = wl if tile == "auto" else f"{wl}_tile{tile}"
+            entry = {"workload": env["desc"], "rounds": rounds, "modes": modes}
+            if wl in ("fp8", "tail", "small256"):
+                entry["problems"] = [{k: r[k] for k in ("M", "N", "K", "mode", "us", "tflops", "frac_peak")}
+                                     for r in table]
+            if wl == "sweep4k":
+                info = pg.pgemm_query_launch(env["h"], 4096, 4096, 4096, env["dt_code"], 1, 0)
+                entry["tile"] = f'{info["bm"]}x{info["bn"]}'
+                entry["tiles"] = info["tiles"]
+                entry["tiles_per_wg_static"] = round(info["tiles"] / info["grid"], 2)
+                entry["per_K_tflops"] = {}
+                for r in table:
+                    entry["per_K_tflops"].setdefault(str(r["K"]), {})[r["mode"]] = r["tflops"]
+            out[key] = entry
+        finally:
+            pg.pgemm_destroy(env["h"])
+        del env
+        torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1",
+                          "n_gpus_requested": args.gpus}))
+        sys.exit(2)
+    if args.oracle_timing:
+        print(json.dumps(oracle_timing()), flush=True)
+        return
+    import numpy as np
+    import torch
+
+    import persistent_tile_scheduling_macro_amd as pg
+    import seeded_inputs as si
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    if args.workload == "uneven":
+        return run_uneven(args, pg, si, torch, np)
+    if args.workload == "custom":
+        add_custom_workload(args)
+    env = setup(pg, torch, si, args, args.workload)
+    desc, dtype, kind, wid, probs = env["desc"], env["dtype"], env["kind"], env["wid"], env["probs"]
+    h, stream, launch, dt_code = env["h"], env["stream"], env["launch"], env["dt_code"]
+    operands, outs = env["operands"], env["outs"]
 
     # warmup
     for _ in range(args.warmup):
@@ -279,28 +467,22 @@ def main():
             launch(p)
             ev[s][i][1].record(stream)
     torch.cuda.synchronize()
+    per = {p: [] for p in probs}
+    for s in range(args.steps):
+        for i, p in enumerate(probs):
+            per[p].append(ev[s][i][0].elapsed_time(ev[s][i][1]) * 1e-3)
 
-    # small-K latency: for K <= 512 the launch and fixed costs dominate, so each such
-    # (K, mode) point is also launched 100 times with an event pair around each launch
-    small_k = {}
-    for p in probs:
-        if p[2] > 512 or args.no_small_k_latency:
-            continue
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(100)]
-        for e0, e1 in evs:
-            e0.record(stream)
-            launch(p)
-            e1.record(stream)
-        torch.cuda.synchronize()
-        us = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
-        small_k.setdefault(f"K={p[2]}", {})[MODE_NAMES[p[3]] + (f"@g{p[4]}" if p[4] else "")] = \
-            {"median_us": round(us[50], 2), "min_us": round(us[0], 2), "max_us": round(us[-1], 2)}
+    # small-K crossover: 100 launches per (K, mode) point in rotated order
+    k_max = args.small_k_max
+    if k_max is None:
+        k_max = {"sweep8k": 2048, "sweep4k": 1024}.get(args.workload, 512)
+    small_k = None if args.no_small_k_latency else small_k_crossover(torch, np, env, k_max)
 
     graph_info = None
     if args.graph:
         # One step captured as a graph: the launches are capture-safe (no memsets; the claiming
         # modes' counter resets itself in the kernel). Replays timed with events on the stream.
-        gstream = torch.cuda.Stream(device=dev)
+        gstream = torch.cuda.Stream(device=torch.device("cuda:0"))
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=gstream):
             pg.pgemm_set_stream(h, gstream)
@@ -321,66 +503,48 @@ def main():
         del g
 
     flops = {p: 2.0 * p[0] * p[1] * p[2] for p in probs}
-    per = {p: [] for p in probs}
-    for s in range(args.steps):
-        for i, p in enumerate(probs):
-            per[p].append(ev[s][i][0].elapsed_time(ev[s][i][1]) * 1e-3)
     step_flops = sum(flops.values())
     value = step_flops * args.steps / wall / 1e12
     peak = PEAK_TFLOPS[dtype]
-
-    table = []
-    for p in probs:
-        m, n, K, mode, gm = p
-        t = float(np.median(per[p]))
-        info = pg.pgemm_query_launch(h, m, n, K, dt_code, mode, gm)
-        byts = ESIZE[dtype] * (m * K + K * n) + 2 * m * n
-        table.append({"M": m, "N": n, "K": K, "mode": MODE_NAMES[mode], "grid_multiple": gm,
-                      "us": round(t * 1e6, 2), "tflops": round(flops[p] / t / 1e12, 1),
-                      "frac_peak": round(flops[p] / t / 1e12 / peak, 4),
-                      "frac_roofline": round(flops[p] / t / 1e12 / min(peak, flops[p] / byts * HBM_GBS / 1e3), 4),
-                      "tile": f'{info["bm"]}x{info["bn"]}', "tiles": info["tiles"], "grid": info["grid"],
-                      "tiles_per_wg": round(info["tiles"] / info["grid"], 2)})
-
-    # roofline of the dominant kernel: the (scheduling mode, macro tile) instance with the
-    # most total time
-    body = {}
-    for p in probs:
+    table, mode_tflops = summarize(env, per, np, peak)
+    for row, p in zip(table, probs):
         info = pg.pgemm_query_launch(h, p[0], p[1], p[2], dt_code, p[3], p[4])
-        body[p] = (p[3], info["bm"] if info["fast_path"] else 0)
+        row.update({"tile": f'{info["bm"]}x{info["bn"]}', "body": info["body"], "tiles": info["tiles"],
+                    "grid": info["grid"], "tiles_per_wg": round(info["tiles"] / info["grid"], 2)})
+
+    # roofline of the dominant kernel: the kernel (dtype, scheduling mode, tile body) with the
+    # most total time over the per-launch pass
+    kname_of = {p: kernel_name(dtype, p[3], pg.pgemm_query_launch(h, p[0], p[1], p[2], dt_code, p[3], p[4]))
+                for p in probs}
     tot = {}
     for p in probs:
-        tot.setdefault(body[p], [0.0, 0.0, 0])
-        tot[body[p]][0] += sum(per[p])
-        tot[body[p]][1] += flops[p] * len(per[p])
-        tot[body[p]][2] += len(per[p])
-    dom = max(tot, key=lambda k: tot[k][0])
-    dom_time, dom_flops, dom_n = tot[dom]
+        tot.setdefault(kname_of[p], [0.0, 0.0, 0])
+        tot[kname_of[p]][0] += sum(per[p])
+        tot[kname_of[p]][1] += flops[p] * len(per[p])
+        tot[kname_of[p]][2] += len(per[p])
+    kname = max(tot, key=lambda k: tot[k][0])
+    dom_time, dom_flops, dom_n = tot[kname]
     achieved = dom_flops / dom_time / 1e12
-    sched_names = {0: "kNonPersistent", 1: "kStatic", 2: "kDynamic", 3: "kCancel", 4: "kStreamK"}
-    dt_name = {"f16": "kF16", "bf16": "kBF16", "e4m3fn": "kF8E4M3"}[dtype]
-    if dom[1]:
-        kname = f"gemm_fast_kernel<{dt_name}, {sched_names[dom[0]]}, kTile{dom[1]}>"
-    else:
-        kname = f"gemm_generic_kernel<{dt_name}, {sched_names[dom[0]]}>"
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": measured_traffic(kname, args.workload),
                 "kernel": kname, "launches": dom_n, "avg_us": round(dom_time / dom_n * 1e6, 2),
                 "flops_per_launch_avg": dom_flops / dom_n,
                 "timing": "HIP events around every launch on the library's stream, in a second pass of "
                           "the same K steps (the timed region itself has no per-launch events)"}
-    if dom[0] == 4:
-        roofline["note"] = "stream-K: each timed run is the GEMM kernel plus its fix-up launch"
+    if any(p[3] == 4 for p in probs if kname_of[p] == kname):
+        roofline["note"] = "stream-K: each timed run is the GEMM kernel plus its tail and fix-up launches"
 
     best = {}
     for row in table:
         key = (row["M"], row["N"], row["K"])
         if key not in best or row["tflops"] > best[key]["tflops"]:
             best[key] = row
-    mode_tflops = {}
-    for mode in sorted({p[3] for p in probs}):
-        ps = [p for p in probs if p[3] == mode]
-        mode_tflops[MODE_NAMES[mode]] = round(sum(flops[p] for p in ps) / sum(float(np.median(per[p])) for p in ps) / 1e12, 1)
+    # the largest problem of the workload (8192^3 for sweep8k), every variant
+    top = max(best, key=lambda k: k[0] * k[1] * k[2])
+    largest = {"problem": f"{top[0]}x{top[1]}x{top[2]}",
+               "variants": {r["mode"] + (f"@g{r['grid_multiple']}" if r["grid_multiple"] else ""):
+                            {"tflops": r["tflops"], "frac_peak": r["frac_peak"], "us": r["us"]}
+                            for r in table if (r["M"], r["N"], r["K"]) == top}}
 
     vendor_info = None
     if args.vendor:
@@ -391,6 +555,12 @@ def main():
         trace_info = tile_trace_summary(pg, h, probs, operands, outs, dt_code, torch, np, args.trace_out)
 
     pg.pgemm_destroy(h)
+    del env, operands, outs
+    torch.cuda.empty_cache()
+
+    configs = None
+    if not args.no_configs and args.workload == "sweep8k" and not args.modes:
+        configs = config_summary(pg, torch, np, si, args)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -401,11 +571,11 @@ def main():
         "value": round(value, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(wall / args.steps * 1e3, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": dtype if dtype != "e4m3fn" else "e4m3fn->bf16", "data": "synthetic",
-        "config": {"workload": desc, "name": args.workload, "tile": args.tile, "b_layout": args.b_layout,
-                   "launches_per_step": len(probs),
-                   "flops_per_step": step_flops},
+        "config": {"workload": desc, "name": args.workload, "tile": args.tile, "mainloop": args.mainloop,
+                   "b_layout": args.b_layout, "launches_per_step": len(probs), "flops_per_step": step_flops},
         "frac_of_peak": round(value / peak, 4),
         "mode_tflops": mode_tflops,
+        "largest_problem": largest,
         "best": {f"{k[0]}x{k[1]}x{k[2]}": {"mode": v["mode"], "tflops": v["tflops"], "frac_peak": v["frac_peak"]}
                  for k, v in sorted(best.items())[-3:]},
         "roofline": roofline,
@@ -414,7 +584,9 @@ def main():
                    "per_launch_pass_ms_per_step": round(sum(sum(v) for v in per.values()) / args.steps * 1e3, 3)},
     }
     if small_k:
-        result["small_k_latency"] = small_k
+        result["small_k_crossover"] = small_k
+    if configs:
+        result["configs"] = configs
     if graph_info:
         result["graph"] = graph_info
     if trace_info:
@@ -648,6 +820,46 @@ def run_uneven(args, pg, si, torch, np):
         with open(args.table, "w") as f:
             json.dump({"result": result, "table": table}, f, indent=1)
     print(json.dumps(result), flush=True)
+
+
+def oracle_timing():
+    """The CPU oracle in full (every row, every column) on each configured problem
+    it finishes in minutes, on all of the host's cores, plus one thread at 256^3.
+    A reported baseline only: seconds and fp64 GFLOP/s per problem."""
+    import numpy as np  # noqa: F401
+
+    import oracle
+    import seeded_inputs as si
+
+    cores = oracle.default_threads()
+    # (label, dtype, input kind, workload id (seeds), M, N, K, K of the drawn operands)
+    plan = [("fp16 256^3", "f16", "uniform", 1, 256, 256, 256, 256)]
+    plan += [(f"fp16 4096^2 x K={K}", "f16", "uniform", 2, 4096, 4096, K, 4096) for K in (128, 1024, 4096)]
+    plan += [(f"fp16 8192^2 x K={K}", "f16", "uniform", 3, 8192, 8192, K, 8192) for K in (256, 2048, 8192)]
+    plan += [("fp8 e4m3 8192^3", "e4m3fn", "uniform", 4, 8192, 8192, 8192, 8192)]
+    plan += [(f"bf16 {n}^3", "bf16", "normal", 5, n, n, n, n) for n in (4000, 6144, 8200)]
+    out = []
+    drawn = {}
+    for label, dtype, kind, wid, M, N, K, kmax in plan:
+        key = (dtype, kind, wid, M, N, kmax)
+        if key not in drawn:
+            drawn.clear()
+            A, B = si.operands(M, N, kmax, dtype, kind, workload=wid)
+            drawn[key] = (A, B)
+        A, B = drawn[key]
+        Ab, Bb = si.bits(A[:, :K].contiguous()), si.bits(B[:K, :].contiguous())
+        t0 = time.perf_counter()
+        oracle.gemm(Ab, Bb, dtype, nthreads=cores)
+        dt = time.perf_counter() - t0
+        out.append({"problem": label, "seconds": round(dt, 3), "gflops_fp64": round(2.0 * M * N * K / dt / 1e9, 2)})
+        print(f"oracle {label}: {dt:.2f} s", file=sys.stderr, flush=True)
+    A1, B1 = si.operands(256, 256, 256, "f16", "uniform", workload=1)
+    t0 = time.perf_counter()
+    oracle.gemm(si.bits(A1), si.bits(B1), "f16", nthreads=1)
+    single = time.perf_counter() - t0
+    return {"oracle_timing": out, "threads": cores, "host_cpus": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0)), "single_thread_256cubed_s": round(single, 4),
+            "kind": "oracle", "what": "fp64 triple loop over the decoded inputs, rows split over threads"}
 
 
 def cpu_baseline(dtype, kind, wid, probs, seconds):

@@ -121,6 +121,31 @@ typedef enum {
   PGEMM_TILE_128 = 2
 } pgemm_tile_t;
 
+/* Wave schedule of the 256 x 256 fast tile (pgemm_set_mainloop). The value
+ * of C does not depend on it: both schedules give every accumulator the same
+ * MFMAs on the same operands in the same order, so C is bitwise the same.
+ * LOCKSTEP: all eight waves of a workgroup copy, read and multiply in step,
+ *   one barrier per k-step; each step's global -> LDS copy is issued right
+ *   after its barrier (the copy/compute overlap of the persistent-kernel
+ *   forum thread's first answer, per workgroup).
+ * PINGPONG: the two waves of each SIMD run opposite phases: while one issues
+ *   copies and reads the next fragments from LDS, the other runs its MFMAs,
+ *   and they swap at each barrier (the same overlap, per SIMD; the load role
+ *   alternates between the waves instead of being given to a producer wave,
+ *   KernelWiki "Persistent Kernels with Cluster Launch Control", tutorial
+ *   note on warp specialization).
+ * AUTO (default): PINGPONG for tiles of at least 20 k-steps of 64 for
+ *   fp16/bf16 (K >= 1217) and 8 k-steps of 128 for fp8 (K >= 897), LOCKSTEP
+ *   below, where its cheaper tile prologue and epilogue win (measured).
+ *   The 128 x 128 tile, the generic body and the split tail of STREAMK
+ *   always run lockstep. The environment variable PGEMM_MAINLOOP (1 or 2)
+ *   overrides the default at pgemm_create. */
+typedef enum {
+  PGEMM_MAINLOOP_AUTO = 0,
+  PGEMM_MAINLOOP_LOCKSTEP = 1,
+  PGEMM_MAINLOOP_PINGPONG = 2
+} pgemm_mainloop_t;
+
 /* Storage of B (pgemm_set_b_layout). The value of C does not depend on it:
  * both layouts feed the MFMAs the same operands in the same order, so C is
  * bitwise the same. */
@@ -131,11 +156,20 @@ typedef enum {
 
 /* Create a handle on HIP device `device` (which becomes current). Allocates
  * the claiming modes' device work counter (zeroed) and caches the CU count.
- * The handle starts on the null stream. *out is NULL on failure. */
+ * The handle starts on the null stream. *out is NULL on failure.
+ * pgemm_create, pgemm_run and pgemm_destroy are this library's stated
+ * interface (the pages specify no API; they fix the operation: forum
+ * thread, question); the other entry points complete it. PGEMM_ERR_INVALID_ARG
+ * for a NULL out or a device outside [0, device count); PGEMM_ERR_OOM if the
+ * handle or the counter cannot be allocated; PGEMM_ERR_HIP if the device
+ * cannot be queried. */
 int pgemm_create(pgemm_handle_t* out, int device);
 
 /* Bind a hipStream_t (passed as void*; NULL = null stream). Later runs
- * enqueue on it. */
+ * enqueue on it; the caller keeps ownership of the stream, which must
+ * outlive its use by the handle. Part of the stated interface's completion
+ * (asynchronous runs on a caller's stream). PGEMM_ERR_INVALID_ARG for a
+ * NULL handle. */
 int pgemm_set_stream(pgemm_handle_t h, void* hip_stream);
 
 /* Enqueue C = A * B on the handle's stream; returns without waiting.
@@ -170,8 +204,9 @@ int pgemm_run(pgemm_handle_t h, const void* A, const void* B, void* C, int64_t M
               int dtype, int sched_mode, int grid_multiple);
 
 /* Wait for the handle's stream, free the work counter, the stream-K
- * workspace and the handle.
- * NULL is accepted (no-op). */
+ * workspace and the handle (stated interface). NULL is accepted (no-op).
+ * Returns PGEMM_ERR_HIP if the wait or a free failed; the handle is freed
+ * either way and must not be used again. */
 int pgemm_destroy(pgemm_handle_t h);
 
 /* pgemm_run with leading dimensions, for operands that are row-major views
@@ -199,11 +234,14 @@ int pgemm_run_ld(pgemm_handle_t h, const void* A, int64_t lda, const void* B, in
  * instead of blocking in a synchronize. */
 int pgemm_wait(pgemm_handle_t h, int timeout_ms);
 
-/* Static text for a status code. */
+/* Static text for a status code (never NULL; unknown codes give
+ * "PGEMM_ERR_UNKNOWN"). Error reporting of the stated interface: every
+ * entry point returns a status instead of raising. */
 const char* pgemm_status_string(int status);
 
-/* Detail of the last failure on this handle ("" if none). Valid until the
- * next call on the handle. */
+/* Detail of the last failure on this handle ("" if none; "invalid handle"
+ * for NULL). Owned by the handle, valid until the next call on it. Error
+ * reporting of the stated interface. */
 const char* pgemm_last_error(pgemm_handle_t h);
 
 /* ---- checking and reporting (not for timed runs) ---------------------- */
@@ -250,12 +288,14 @@ int pgemm_clock_khz(int device, int* khz);
 
 /* Report how pgemm_run would launch this problem, without launching:
  * tile count, grid size, occupancy (workgroups per CU), macro tile
- * (bm x bn, k-step bk in elements), and whether the fast kernel is used.
- * Output pointers may be NULL. Alignment is judged from the sizes only
- * (pointers assumed 16-byte aligned). */
+ * (bm x bn, k-step bk in elements), and the tile body of the launch that
+ * computes the whole tiles: 0 = the generic kernel (unaligned sizes),
+ * 1 = the fast kernel with lockstep waves, 2 = the fast kernel in ping-pong
+ * (pgemm_mainloop_t). Output pointers may be NULL. Alignment is judged from
+ * the sizes only (pointers assumed 16-byte aligned). */
 int pgemm_query_launch(pgemm_handle_t h, int64_t M, int64_t N, int64_t K, int dtype, int sched_mode,
                        int grid_multiple, int* tiles, int* grid, int* occupancy, int* bm, int* bn, int* bk,
-                       int* fast_path);
+                       int* body);
 
 /* Report the STREAMK split pgemm_run would use for this problem, without
  * launching: whole_tiles = W*G tiles run whole, split_tiles = R tail
@@ -291,6 +331,11 @@ int pgemm_set_tile_config(pgemm_handle_t h, int tile);
  * dtypes ignore the scales. PGEMM_ERR_INVALID_ARG for a NULL handle, a
  * non-finite scale or a non-finite product. */
 int pgemm_set_fp8_scales(pgemm_handle_t h, float scale_a, float scale_b);
+
+/* Choose the wave schedule of the 256 x 256 tile for later runs on this
+ * handle (pgemm_mainloop_t; C's bits do not depend on it). Returns
+ * PGEMM_ERR_INVALID_ARG for a NULL handle or an unknown value. */
+int pgemm_set_mainloop(pgemm_handle_t h, int mainloop);
 
 /* Choose how B is stored for later runs on this handle (pgemm_b_layout_t;
  * default PGEMM_B_KN). With PGEMM_B_NK the fast kernel copies B's tile like

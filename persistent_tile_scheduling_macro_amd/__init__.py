@@ -38,6 +38,10 @@ PGEMM_TILE_128 = 2
 PGEMM_B_KN = 0
 PGEMM_B_NK = 1
 
+PGEMM_MAINLOOP_AUTO = 0
+PGEMM_MAINLOOP_LOCKSTEP = 1
+PGEMM_MAINLOOP_PINGPONG = 2
+
 DTYPE_NAMES = {"f16": PGEMM_F16, "bf16": PGEMM_BF16, "e4m3fn": PGEMM_F8E4M3_BF16}
 SCHED_NAMES = {"nonpersistent": PGEMM_SCHED_NONPERSISTENT, "static": PGEMM_SCHED_STATIC,
                "dynamic": PGEMM_SCHED_DYNAMIC, "cancel": PGEMM_SCHED_CANCEL, "streamk": PGEMM_SCHED_STREAMK}
@@ -77,6 +81,7 @@ _query_streamk = _sig("pgemm_query_streamk", _int, _vp, _i64, _i64, _i64, _int, 
 _set_tile_order = _sig("pgemm_set_tile_order", _int, _vp, _int, _int)
 _set_tile_config = _sig("pgemm_set_tile_config", _int, _vp, _int)
 _set_b_layout = _sig("pgemm_set_b_layout", _int, _vp, _int)
+_set_mainloop = _sig("pgemm_set_mainloop", _int, _vp, _int)
 _set_fp8_scales = _sig("pgemm_set_fp8_scales", _int, _vp, ctypes.c_float, ctypes.c_float)
 _tile_coords = _sig("pgemm_tile_coords", _int, _i64, _i64, _i64, _int, _int, _ip, _ip)
 _read_work_counter = _sig("pgemm_read_work_counter", _int, _vp, ctypes.POINTER(_i32))
@@ -184,8 +189,10 @@ def pgemm_query_launch(h, M: int, N: int, K: int, dtype: int, sched_mode: int, g
     out = [ctypes.c_int() for _ in range(7)]
     _check(_query_launch(h, int(M), int(N), int(K), int(dtype), int(sched_mode), int(grid_multiple),
                          *[ctypes.byref(o) for o in out]), h)
-    keys = ["tiles", "grid", "occupancy", "bm", "bn", "bk", "fast_path"]
-    return {k: o.value for k, o in zip(keys, out)}
+    keys = ["tiles", "grid", "occupancy", "bm", "bn", "bk", "body"]
+    d = {k: o.value for k, o in zip(keys, out)}
+    d["fast_path"] = int(d["body"] != 0)  # 0: generic kernel; body 1 lockstep, 2 ping-pong
+    return d
 
 
 def pgemm_query_streamk(h, M: int, N: int, K: int, dtype: int, grid_multiple: int = 0) -> dict:
@@ -210,6 +217,11 @@ def pgemm_set_tile_order(h, group_m: int = 8, xcd_remap=True) -> None:
 
 def pgemm_set_tile_config(h, tile: int) -> None:
     _check(_set_tile_config(h, int(tile)), h)
+
+
+def pgemm_set_mainloop(h, mainloop: int) -> None:
+    """Wave schedule of the 256 x 256 tile: PGEMM_MAINLOOP_AUTO, _LOCKSTEP or _PINGPONG."""
+    _check(_set_mainloop(h, int(mainloop)), h)
 
 
 def pgemm_set_fp8_scales(h, scale_a: float, scale_b: float) -> None:

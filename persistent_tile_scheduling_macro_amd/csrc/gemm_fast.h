@@ -366,7 +366,13 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, Tile<CFG>::MIN_WAVES_PE
   int p_mrem = 0, p_krem = 0, p_nrem = 0;
   const uint32_t a_base = (uint32_t)a_row0 * (uint32_t)lda + 16u * (uint32_t)a_chunk;
   int p_kt = 0, p_ke = 0; // stream-K: next step, end of the unit's k-step range
+  // Row strides and the wave's LDS block column, made opaque at each step so the
+  // per-instruction offsets and LDS destinations are recomputed from them with
+  // one scalar operation each instead of being hoisted out of the loop as some
+  // two dozen loop invariants (which exhaust the SGPRs and push values to VGPRs).
+  int lda_s = (int)lda, ldb_s = (int)ldb, wv_s = wave * 1024;
   auto begin_copy = [&]() __attribute__((always_inline)) {
+    asm volatile("" : "+s"(lda_s), "+s"(ldb_s), "+s"(wv_s));
     if (p_done) return;
     int kt;
     if constexpr (SK) {
@@ -406,24 +412,26 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, Tile<CFG>::MIN_WAVES_PE
   auto copy_part = [&](uint8_t* sA, uint8_t* sB, auto jc) __attribute__((always_inline)) {
     constexpr int J = decltype(jc)::value;
     if (!p_busy) return;
+    // per-lane base in voffset (kOOB when masked), the instruction's row offset in soffset
     if constexpr (J < LA) {
       const bool ok = p_kval & (a_row0 + 8 * WAVES * J < p_mrem);
-      const uint32_t off = ok ? a_base + (uint32_t)(8 * WAVES * J) * (uint32_t)lda : kOOB;
-      load16_to_lds(ra, sA + (wave + WAVES * J) * 1024, off);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, PGEMM_LDS(void, sA + WAVES * J * 1024 + wv_s), 16, ok ? a_base : kOOB,
+                                               8 * WAVES * J * lda_s, 0, 0);
     } else {
       constexpr int JB = J - LA;
       if constexpr (BT) {
         // rows n of N x K B, copied like A's rows m (same lanes, chunks and swizzle)
         const bool ok = p_kval & (a_row0 + 8 * WAVES * JB < p_nrem);
-        const uint32_t off = ok ? ((uint32_t)a_row0 + (uint32_t)(8 * WAVES * JB)) * (uint32_t)ldb + 16u * (uint32_t)a_chunk
-                                : kOOB;
-        load16_to_lds(rb, sB + (wave + WAVES * JB) * 1024, off);
+        const uint32_t base = (uint32_t)a_row0 * (uint32_t)ldb + 16u * (uint32_t)a_chunk;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, PGEMM_LDS(void, sB + WAVES * JB * 1024 + wv_s), 16, ok ? base : kOOB,
+                                                 8 * WAVES * JB * ldb_s, 0, 0);
       } else {
         const int row = b_row0 + B_RPI * WAVES * JB;
         const int Lc = b_chunk0 ^ b_swz<ES, B_ROW>(B_RPI * WAVES * JB);
         const bool ok = (row < p_krem) & (16 * Lc < p_nrem);
-        const uint32_t off = ok ? (uint32_t)row * (uint32_t)ldb + 16u * (uint32_t)Lc : kOOB;
-        load16_to_lds(rb, sB + (wave + WAVES * JB) * 1024, off);
+        const uint32_t base = (uint32_t)b_row0 * (uint32_t)ldb + 16u * (uint32_t)Lc;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, PGEMM_LDS(void, sB + WAVES * JB * 1024 + wv_s), 16, ok ? base : kOOB,
+                                                 B_RPI * WAVES * JB * ldb_s, 0, 0);
       }
     }
     if (J == L - 1) p_busy = false;
@@ -518,12 +526,13 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, Tile<CFG>::MIN_WAVES_PE
           for (int nb = 0; nb < NB; ++nb) {
             const int n = ncol + nb * 16;
             out_t* dst = C + (int64_t)m * ldc + n;
+            const floatx4_t v = acc_read(acc[mb][nb]) * cs;
             if (n + 3 < N) {
-              store4(dst, acc_read(acc[mb][nb]) * cs);
+              store4(dst, v);
             } else {
 #pragma unroll
               for (int e = 0; e < 4; ++e)
-                if (n + e < N) dst[e] = to_out(acc[mb][nb][e] * cs, (out_t*)nullptr);
+                if (n + e < N) dst[e] = to_out(v[e], (out_t*)nullptr);
             }
           }
         }

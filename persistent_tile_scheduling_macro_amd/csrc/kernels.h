@@ -8,8 +8,11 @@ namespace pgemm {
 typedef void (*kernel_fn)(Params);
 
 // Tile body of a launch: the fast kernel in one of its two macro-tile
-// configurations, or the generic 64 x 64 body for unaligned operands.
-enum Body : int { kBodyGeneric = 0, kBodyTile256 = 1, kBodyTile128 = 2 };
+// configurations (lockstep waves), the 256 x 256 ping-pong form of the fast
+// kernel (gemm_pingpong.h), or the generic 64 x 64 body for unaligned
+// operands.
+enum Body : int { kBodyGeneric = 0, kBodyTile256 = 1, kBodyTile128 = 2, kBodyPingPong = 3 };
+constexpr int kNumBodies = 4;
 
 // Returns the kernel for (scheduling mode, tile body); `trace` selects the
 // fast bodies' instantiation that writes the tile trace, `bt` the one that
@@ -17,6 +20,13 @@ enum Body : int { kBodyGeneric = 0, kBodyTile256 = 1, kBodyTile128 = 2 };
 kernel_fn pick_kernel_f16(int sched, int body, bool trace, bool bt);
 kernel_fn pick_kernel_bf16(int sched, int body, bool trace, bool bt);
 kernel_fn pick_kernel_f8(int sched, int body, bool trace, bool bt);
+
+// The ping-pong 256 x 256 kernel for the non-persistent, static, dynamic and
+// cancel-and-reuse modes (kernels_pp_*.hip); nullptr for stream-K, whose
+// tail launch takes the lockstep 256 x 256 body.
+kernel_fn pick_kernel_pp_f16(int sched, bool trace, bool bt);
+kernel_fn pick_kernel_pp_bf16(int sched, bool trace, bool bt);
+kernel_fn pick_kernel_pp_f8(int sched, bool trace, bool bt);
 
 // The stream-K fix-up kernel of a fast tile body (nullptr for the generic body).
 kernel_fn pick_fixup_f16(int body);

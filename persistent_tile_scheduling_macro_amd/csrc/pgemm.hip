@@ -41,12 +41,13 @@ struct pgemm_ctx {
   int group_m = 4;
   int xcd_remap = -1;
   int tile = PGEMM_TILE_AUTO; // macro-tile choice of the fast kernel
+  int mainloop = PGEMM_MAINLOOP_AUTO; // lockstep or ping-pong waves for the 256 x 256 tile
   // Stream-K: shortest piece, in k-step pairs, a split may cut (tiles with
   // fewer pairs are not split).
   int sk_min_pairs = 4;
   float* work = nullptr; // stream-K partial tiles, grown on demand
   size_t work_bytes = 0;
-  int occ_cache[3][5][3] = {}; // occupancy per (dtype, mode, body); 0 = not queried yet
+  int occ_cache[3][5][kNumBodies] = {}; // occupancy per (dtype, mode, body); 0 = not queried yet
   char last_error[512] = {0};
 };
 
@@ -69,7 +70,8 @@ struct BodyShape {
 };
 BodyShape body_shape(int body) {
   switch (body) {
-    case kBodyTile256: return {256, 256, 512};
+    case kBodyTile256:
+    case kBodyPingPong: return {256, 256, 512};
     case kBodyTile128: return {128, 128, 256};
     default: return {64, 64, 256};
   }
@@ -77,6 +79,15 @@ BodyShape body_shape(int body) {
 int fast_block_k(int dtype) { return dtype == kF8E4M3 ? 128 : 64; }
 
 kernel_fn pick_kernel(int dtype, int sched, int body, bool trace = false, bool bt = false) {
+  if (body == kBodyPingPong) {
+    // stream-K's tail launch takes the lockstep body (its whole waves run as a static launch)
+    if (sched == kStreamK) return pick_kernel(dtype, sched, kBodyTile256, trace, bt);
+    switch (dtype) {
+      case kF16: return pick_kernel_pp_f16(sched, trace, bt);
+      case kBF16: return pick_kernel_pp_bf16(sched, trace, bt);
+      default: return pick_kernel_pp_f8(sched, trace, bt);
+    }
+  }
   switch (dtype) {
     case kF16: return pick_kernel_f16(sched, body, trace, bt);
     case kBF16: return pick_kernel_bf16(sched, body, trace, bt);
@@ -85,6 +96,7 @@ kernel_fn pick_kernel(int dtype, int sched, int body, bool trace = false, bool b
 }
 
 kernel_fn pick_fixup(int dtype, int body) {
+  if (body == kBodyPingPong) body = kBodyTile256; // same tile geometry
   switch (dtype) {
     case kF16: return pick_fixup_f16(body);
     case kBF16: return pick_fixup_bf16(body);
@@ -96,13 +108,32 @@ kernel_fn pick_fixup(int dtype, int body) {
 // moves the fewest operand bytes per flop and measured faster whenever it
 // gives every CU a tile (4096^2 to 8200^2, every K); when it would leave CUs
 // idle, the 128 x 128 tile (two workgroups per CU, four times the tiles)
-// fills the chip.
-int choose_body(const pgemm_ctx* h, int64_t M, int64_t N, bool fast) {
+// fills the chip. The 256 x 256 tile runs its waves in ping-pong (each
+// SIMD's two waves in opposite copy/compute phases) once a tile has enough
+// k-steps; shorter k-loops take the lockstep form, whose tile prologue and
+// epilogue cost less. Measured per K on MI355X (M = N = 4096 and 8192, every
+// scheduling mode): 16-bit ping-pong is 2-17% slower up to 16 k-steps
+// (K <= 1024), level at 18-20 and 2-14% faster from there; fp8 ping-pong is
+// already 10% faster at 8 k-steps (8192^2 x 1024) and 2-3% slower at 2.
+constexpr int kPingPongMinSteps16 = 20; // fp16 / bf16: K >= 1217
+constexpr int kPingPongMinSteps8 = 8;   // e4m3: K >= 897
+
+int choose_body(const pgemm_ctx* h, int64_t M, int64_t N, int64_t K, int dtype, bool fast) {
   if (!fast) return kBodyGeneric;
-  if (h->tile == PGEMM_TILE_256) return kBodyTile256;
-  if (h->tile == PGEMM_TILE_128) return kBodyTile128;
-  const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
-  return t256 < (int64_t)h->cus ? kBodyTile128 : kBodyTile256;
+  int body;
+  if (h->tile == PGEMM_TILE_256) {
+    body = kBodyTile256;
+  } else if (h->tile == PGEMM_TILE_128) {
+    body = kBodyTile128;
+  } else {
+    const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+    body = t256 < (int64_t)h->cus ? kBodyTile128 : kBodyTile256;
+  }
+  if (body != kBodyTile256 || h->mainloop == PGEMM_MAINLOOP_LOCKSTEP) return body;
+  if (h->mainloop == PGEMM_MAINLOOP_PINGPONG) return kBodyPingPong;
+  const int64_t bk = dtype == kF8E4M3 ? 128 : 64;
+  const int64_t nk = ((K + bk - 1) / bk + 1) & ~(int64_t)1;
+  return nk >= (dtype == kF8E4M3 ? kPingPongMinSteps8 : kPingPongMinSteps16) ? kBodyPingPong : kBodyTile256;
 }
 
 int esize_of(int dtype) { return dtype == kF8E4M3 ? 1 : 2; }
@@ -159,7 +190,7 @@ void plan_streamk(const pgemm_ctx* h, int64_t K, int64_t G_full, Plan* pl) {
 int plan_launch(pgemm_ctx* h, int64_t M, int64_t N, int64_t K, int dtype, int sched, int grid_multiple,
                 bool fast, Plan* pl) {
   pl->fast = fast;
-  pl->body = choose_body(h, M, N, fast);
+  pl->body = choose_body(h, M, N, K, dtype, fast);
   const BodyShape bs = body_shape(pl->body);
   pl->threads = bs.threads;
   pl->bm = bs.bm;
@@ -251,6 +282,10 @@ int pgemm_create(pgemm_handle_t* out, int device) {
   if (const char* t = getenv("PGEMM_TILE")) {
     const int v = atoi(t);
     h->tile = v == 256 ? PGEMM_TILE_256 : v == 128 ? PGEMM_TILE_128 : PGEMM_TILE_AUTO;
+  }
+  if (const char* m = getenv("PGEMM_MAINLOOP")) {
+    const int v = atoi(m);
+    h->mainloop = v == PGEMM_MAINLOOP_LOCKSTEP || v == PGEMM_MAINLOOP_PINGPONG ? v : PGEMM_MAINLOOP_AUTO;
   }
   *out = h;
   return PGEMM_OK;
@@ -487,7 +522,7 @@ int pgemm_clock_khz(int device, int* khz) {
 
 int pgemm_query_launch(pgemm_handle_t h, int64_t M, int64_t N, int64_t K, int dtype, int sched_mode,
                        int grid_multiple, int* tiles, int* grid, int* occupancy, int* bm, int* bn, int* bk,
-                       int* fast_path) {
+                       int* body) {
   int rc = check_common(h, M, N, K, dtype, sched_mode);
   if (rc != PGEMM_OK) return rc;
   // the plan may query the kernel's occupancy: on the handle's device
@@ -501,7 +536,10 @@ int pgemm_query_launch(pgemm_handle_t h, int64_t M, int64_t N, int64_t K, int dt
   if (bm) *bm = pl.bm;
   if (bn) *bn = pl.bn;
   if (bk) *bk = pl.bk;
-  if (fast_path) *fast_path = pl.fast ? 1 : 0;
+  if (body) {
+    // the tile body of the launch that does the GEMM's whole tiles: 0 generic, 1 lockstep, 2 ping-pong
+    *body = !pl.fast ? 0 : pl.body == kBodyPingPong ? 2 : 1;
+  }
   return PGEMM_OK;
 }
 
@@ -534,6 +572,14 @@ int pgemm_set_tile_config(pgemm_handle_t h, int tile) {
   if (!h) return PGEMM_ERR_INVALID_ARG;
   if (tile < PGEMM_TILE_AUTO || tile > PGEMM_TILE_128) return fail(h, PGEMM_ERR_INVALID_ARG, "unknown tile config %d", tile);
   h->tile = tile;
+  return PGEMM_OK;
+}
+
+int pgemm_set_mainloop(pgemm_handle_t h, int mainloop) {
+  if (!h) return PGEMM_ERR_INVALID_ARG;
+  if (mainloop < PGEMM_MAINLOOP_AUTO || mainloop > PGEMM_MAINLOOP_PINGPONG)
+    return fail(h, PGEMM_ERR_INVALID_ARG, "unknown mainloop %d", mainloop);
+  h->mainloop = mainloop;
   return PGEMM_OK;
 }
 

@@ -160,3 +160,47 @@ def test_fp8_scales_argument_checks(pg):
     with pytest.raises(pg.PgemmError) as e:
         pg.pgemm_set_fp8_scales(None, 1.0, 1.0)
     assert e.value.status == pg.PGEMM_ERR_INVALID_ARG
+
+
+def _build_module():
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "_pgemm_build", os.path.join(ROOT, "persistent_tile_scheduling_macro_amd", "build.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    return b
+
+
+def test_resource_remark_parser_and_trace_flag():
+    """The build collects hipcc's per-kernel resource remarks; the parser reads every field and
+    tells the tile-trace instantiations (first bool template argument true) from the timed ones."""
+    b = _build_module()
+    text = "\n".join([
+        "./x.h:1:1: remark: Function Name: _ZN5pgemm2pp14gemm_pp_kernelILi0ELi1ELb0ELb1EEEvNS_6ParamsE [-Rpass]",
+        "./x.h:1:1: remark:     TotalSGPRs: 101 [-Rpass]", "./x.h:1:1: remark:     VGPRs: 126 [-Rpass]",
+        "./x.h:1:1: remark:     AGPRs: 128 [-Rpass]", "./x.h:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass]",
+        "./x.h:1:1: remark:     Occupancy [waves/SIMD]: 2 [-Rpass]",
+        "./x.h:1:1: remark:     LDS Size [bytes/block]: 131072 [-Rpass]",
+        "./x.h:1:1: remark: Function Name: _ZN5pgemm4fast16gemm_fast_kernelILi0ELi3ELi0ELb1ELb0EEEvNS_6ParamsE",
+        "./x.h:1:1: remark:     ScratchSize [bytes/lane]: 12 [-Rpass]"])
+    ks = b.parse_resource_remarks(text)
+    assert ks[0] == {"name": "_ZN5pgemm2pp14gemm_pp_kernelILi0ELi1ELb0ELb1EEEvNS_6ParamsE", "sgpr": 101, "vgpr": 126,
+                     "agpr": 128, "scratch": 0, "occupancy": 2, "lds": 131072}
+    assert ks[1]["scratch"] == 12
+    assert not b.is_traced(ks[0]["name"]) and b.is_traced(ks[1]["name"])
+    assert not b.is_traced("_ZN5pgemm7generic19gemm_generic_kernelILi0ELi1EEEvNS_6ParamsE")
+
+
+def test_built_kernels_do_not_spill():
+    """Report written by the last build: no kernel that timed runs launch uses scratch memory,
+    and every fast kernel fits two waves per SIMD."""
+    path = os.path.join(ROOT, "persistent_tile_scheduling_macro_amd", "_build", "kernel_resources.txt")
+    if not os.path.exists(path):
+        pytest.skip("no build report (run the build first)")
+    rows = [l.split() for l in open(path) if not l.startswith("#")]
+    assert len(rows) > 100
+    for name, vgpr, agpr, sgpr, scratch, occ, lds, traced in rows:
+        if traced == "0":
+            assert int(scratch) == 0, name
+        if "gemm_fast_kernel" in name or "gemm_pp_kernel" in name:
+            assert int(occ) >= 2 and int(vgpr) >= 0, name

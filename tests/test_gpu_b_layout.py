@@ -22,7 +22,8 @@ pytestmark = pytest.mark.gpu
 DT = {"f16": 0, "bf16": 1, "e4m3fn": 2}
 OUT = {"f16": ("f16", torch.float16), "bf16": ("bf16", torch.bfloat16), "e4m3fn": ("bf16", torch.bfloat16)}
 TOL = {"f16": 2e-3, "bf16": 2e-3, "e4m3fn": 1e-2}
-TILES = {"t256": 1, "t128": 2}
+# (tile config, mainloop): the 256 x 256 tile with lockstep waves and in ping-pong, and 128 x 128
+TILES = {"t256_lockstep": (1, 1), "t256_pingpong": (1, 2), "t128": (2, 0)}
 
 
 @pytest.fixture(scope="module")
@@ -37,7 +38,8 @@ def pg():
 def handles(pg, request):
     kn, nk = pg.pgemm_create(0), pg.pgemm_create(0)
     for h in (kn, nk):
-        pg.pgemm_set_tile_config(h, TILES[request.param])
+        pg.pgemm_set_tile_config(h, TILES[request.param][0])
+    pg.pgemm_set_mainloop(h, TILES[request.param][1])
     pg.pgemm_set_b_layout(nk, pg.PGEMM_B_NK)
     yield kn, nk
     pg.pgemm_destroy(kn)

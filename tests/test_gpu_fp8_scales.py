@@ -20,7 +20,8 @@ import seeded_inputs as si
 
 pytestmark = pytest.mark.gpu
 
-TILES = {"t256": 1, "t128": 2}
+# (tile config, mainloop): the 256 x 256 tile with lockstep waves and in ping-pong, and 128 x 128
+TILES = {"t256_lockstep": (1, 1), "t256_pingpong": (1, 2), "t128": (2, 0)}
 F8 = 2
 
 
@@ -35,7 +36,8 @@ def pg():
 @pytest.fixture(scope="module", params=sorted(TILES))
 def handle(pg, request):
     h = pg.pgemm_create(0)
-    pg.pgemm_set_tile_config(h, TILES[request.param])
+    pg.pgemm_set_tile_config(h, TILES[request.param][0])
+    pg.pgemm_set_mainloop(h, TILES[request.param][1])
     yield h
     pg.pgemm_set_fp8_scales(h, 1.0, 1.0)
     pg.pgemm_destroy(h)

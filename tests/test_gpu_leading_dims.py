@@ -19,7 +19,8 @@ import seeded_inputs as si
 pytestmark = pytest.mark.gpu
 
 DT = {"f16": (0, torch.float16), "bf16": (1, torch.bfloat16), "e4m3fn": (2, torch.bfloat16)}
-TILES = {"t256": 1, "t128": 2}
+# (tile config, mainloop): the 256 x 256 tile with lockstep waves and in ping-pong, and 128 x 128
+TILES = {"t256_lockstep": (1, 1), "t256_pingpong": (1, 2), "t128": (2, 0)}
 SENT = 5.0  # padding sentinel, exact in fp16 and bf16
 
 
@@ -34,7 +35,8 @@ def pg():
 @pytest.fixture(scope="module", params=sorted(TILES))
 def handle(pg, request):
     h = pg.pgemm_create(0)
-    pg.pgemm_set_tile_config(h, TILES[request.param])
+    pg.pgemm_set_tile_config(h, TILES[request.param][0])
+    pg.pgemm_set_mainloop(h, TILES[request.param][1])
     yield h
     pg.pgemm_set_b_layout(h, pg.PGEMM_B_KN)
     pg.pgemm_destroy(h)

@@ -28,7 +28,8 @@ OUT = {"f16": ("f16", torch.float16), "bf16": ("bf16", torch.bfloat16), "e4m3fn"
 TOL = {"f16": 2e-3, "bf16": 2e-3, "e4m3fn": 1e-2}
 MODES = [0, 1, 2, 3, 4]  # non-persistent, static, dynamic, cancel-and-reuse, stream-K
 SAME_BITS = [0, 1, 2, 3]  # modes that run every tile whole: C bitwise identical
-TILES = {"t256": 1, "t128": 2}  # PGEMM_TILE_256, PGEMM_TILE_128
+# (tile config, mainloop): the 256 x 256 tile with lockstep waves and in ping-pong, and 128 x 128
+TILES = {"t256_lockstep": (1, 1), "t256_pingpong": (1, 2), "t128": (2, 0)}
 
 
 @pytest.fixture(scope="module")
@@ -42,7 +43,8 @@ def pg():
 @pytest.fixture(scope="module", params=sorted(TILES))
 def handle(pg, request):
     h = pg.pgemm_create(0)
-    pg.pgemm_set_tile_config(h, TILES[request.param])
+    pg.pgemm_set_tile_config(h, TILES[request.param][0])
+    pg.pgemm_set_mainloop(h, TILES[request.param][1])
     yield h
     pg.pgemm_destroy(h)
 

@@ -62,11 +62,15 @@ def pg():
 
 @pytest.fixture(scope="module")
 def handles(pg):
+    """One handle per (tile, mainloop): the automatic wave schedule (ping-pong for the whole
+    waves of long k-loops) and lockstep waves forced."""
     hs = {}
     for tile, code in TILES.items():
-        h = pg.pgemm_create(0)
-        pg.pgemm_set_tile_config(h, code)
-        hs[tile] = h
+        for ml in (0, 1):
+            h = pg.pgemm_create(0)
+            pg.pgemm_set_tile_config(h, code)
+            pg.pgemm_set_mainloop(h, ml)
+            hs[(tile, ml)] = h
     yield hs
     for h in hs.values():
         pg.pgemm_destroy(h)
@@ -96,10 +100,11 @@ def run_sk(pg, h, Ad, Bd, M, N, K, dtype, gm, log=True):
     return C, info, (visits.cpu().numpy() if log else None), (owner.cpu().numpy() if log else None)
 
 
+@pytest.mark.parametrize("mainloop", [0, 1], ids=["auto", "lockstep"])
 @pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-{c[1]}x{c[2]}x{c[3]}-t{c[4]}-g{c[5]}" for c in CASES])
-def test_streamk_parity(pg, handles, case):
+def test_streamk_parity(pg, handles, case, mainloop):
     dtype, M, N, K, tile, gm, what = case
-    h = handles[tile]
+    h = handles[(tile, mainloop)]
     dev = torch.device("cuda:0")
     split = pg.pgemm_query_streamk(h, M, N, K, DT[dtype], gm)
     info = pg.pgemm_query_launch(h, M, N, K, DT[dtype], SK, gm)
