@@ -209,6 +209,26 @@ int pgemm_run(pgemm_handle_t h, const void* A, const void* B, void* C, int64_t M
  * either way and must not be used again. */
 int pgemm_destroy(pgemm_handle_t h);
 
+/* Size in bytes of the device scratch that pgemm_run_noalloc uses for
+ * STREAMK partial tiles (one copy per device, held until the process ends). */
+#define PGEMM_NOALLOC_SCRATCH_BYTES (96u << 20)
+
+/* pgemm_run that allocates nothing, for callers that cannot call hipMalloc
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation). Same arguments, semantics, errors and results (bitwise) as
+ * pgemm_run, except for where STREAMK keeps its fp32 partial tiles: in a
+ * file-scope device array of PGEMM_NOALLOC_SCRATCH_BYTES per device (set up
+ * by pgemm_create on the handle's device), not in the handle's workspace.
+ * A STREAMK split that needs more (pgemm_query_streamk's workspace_bytes)
+ * fails with PGEMM_ERR_UNSUPPORTED before any launch; no other mode needs
+ * scratch. The partial tiles are fully written before they are read, so the
+ * array needs no clearing between calls. All calls on one device share its
+ * array: two STREAMK calls whose work overlaps on the device (on different
+ * streams, or different handles) race on it; serialize them (one stream).
+ * The call makes no hipMalloc, hipFree or stream synchronization. */
+int pgemm_run_noalloc(pgemm_handle_t h, const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                      int dtype, int sched_mode, int grid_multiple);
+
 /* pgemm_run with leading dimensions, for operands that are row-major views
  * inside larger allocations: A[i][k] at A + i*lda + k, B[k][n] at
  * B + k*ldb + n (or, with PGEMM_B_NK, at B + n*ldb + k), C[i][j] at

@@ -65,6 +65,7 @@ def _sig(name, restype, *argtypes):
 _create = _sig("pgemm_create", _int, ctypes.POINTER(_vp), _int)
 _set_stream = _sig("pgemm_set_stream", _int, _vp, _vp)
 _run = _sig("pgemm_run", _int, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int)
+_run_noalloc = _sig("pgemm_run_noalloc", _int, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int)
 _run_ld = _sig("pgemm_run_ld", _int, _vp, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _int, _int, _int)
 _destroy = _sig("pgemm_destroy", _int, _vp)
 _status_string = _sig("pgemm_status_string", ctypes.c_char_p, _int)
@@ -140,6 +141,16 @@ def pgemm_run(h, A, B, C, M: int, N: int, K: int, dtype: int, sched_mode: int, g
     """Enqueue C = A @ B (device pointers or tensors) on the handle's stream."""
     _check(_run(h, _ptr(A), _ptr(B), _ptr(C), int(M), int(N), int(K), int(dtype), int(sched_mode),
                 int(grid_multiple)), h)
+
+
+def pgemm_run_noalloc(h, A, B, C, M: int, N: int, K: int, dtype: int, sched_mode: int,
+                      grid_multiple: int = 0) -> None:
+    """pgemm_run that allocates nothing (stream-K partial tiles in the device's fixed scratch)."""
+    _check(_run_noalloc(h, _ptr(A), _ptr(B), _ptr(C), int(M), int(N), int(K), int(dtype), int(sched_mode),
+                        int(grid_multiple)), h)
+
+
+PGEMM_NOALLOC_SCRATCH_BYTES = 96 << 20
 
 
 def pgemm_run_ld(h, A, lda: int, B, ldb: int, C, ldc: int, M: int, N: int, K: int, dtype: int,

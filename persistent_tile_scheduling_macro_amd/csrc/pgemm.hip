@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <chrono>
 #include <cmath>
+#include <mutex>
 #include <thread>
 #include <cstdarg>
 #include <cstdio>
@@ -50,6 +51,42 @@ struct pgemm_ctx {
   int occ_cache[3][5][kNumBodies] = {}; // occupancy per (dtype, mode, body); 0 = not queried yet
   char last_error[512] = {0};
 };
+
+// ---- device scratch of the allocation-free entry point -----------------------------
+// pgemm_run_noalloc takes the stream-K partial tiles from this file-scope array
+// instead of a workspace the handle grows with hipMalloc. Each device that the
+// library runs on holds its own copy until the process ends. In host code
+// `scratch` is only a host-side stand-in for the symbol: its device address is
+// looked up once per device (hipGetSymbolAddress, in pgemm_create) and only that
+// address is ever handed to kernels.
+static __device__ __align__(256) float scratch[PGEMM_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+float* g_scratch[kMaxDevices] = {}; // device address of `scratch` per device id
+
+// With `device` current: look up its copy of `scratch` once.
+hipError_t scratch_setup(int device) {
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[device]) return hipSuccess;
+  void* ptr = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  if (!ptr) return hipErrorInvalidSymbol;
+  g_scratch[device] = static_cast<float*>(ptr);
+  return hipSuccess;
+}
+
+float* scratch_of(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  return g_scratch[device];
+}
+
+} // namespace
 
 namespace {
 
@@ -252,6 +289,11 @@ int check_common(pgemm_ctx* h, int64_t M, int64_t N, int64_t K, int dtype, int s
 
 } // namespace
 
+namespace {
+int run_impl(pgemm_handle_t h, const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+             int64_t M, int64_t N, int64_t K, int dtype, int sched_mode, int grid_multiple, bool noalloc);
+} // namespace
+
 extern "C" {
 
 int pgemm_create(pgemm_handle_t* out, int device) {
@@ -272,6 +314,12 @@ int pgemm_create(pgemm_handle_t* out, int device) {
     return PGEMM_ERR_OOM;
   }
   if (hipMemset(h->counter, 0, 256) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    (void)hipFree(h->counter);
+    delete h;
+    return PGEMM_ERR_HIP;
+  }
+  if (scratch_setup(device) != hipSuccess) { // the allocation-free entry point's device scratch
+    (void)hipGetLastError();
     (void)hipFree(h->counter);
     delete h;
     return PGEMM_ERR_HIP;
@@ -305,6 +353,23 @@ int pgemm_run(pgemm_handle_t h, const void* A, const void* B, void* C, int64_t M
 
 int pgemm_run_ld(pgemm_handle_t h, const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
                  int64_t M, int64_t N, int64_t K, int dtype, int sched_mode, int grid_multiple) {
+  return run_impl(h, A, lda, B, ldb, C, ldc, M, N, K, dtype, sched_mode, grid_multiple, false);
+}
+
+int pgemm_run_noalloc(pgemm_handle_t h, const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                      int dtype, int sched_mode, int grid_multiple) {
+  if (!h) return PGEMM_ERR_INVALID_ARG;
+  return run_impl(h, A, K, B, h->b_nk ? K : N, C, N, M, N, K, dtype, sched_mode, grid_multiple, true);
+}
+
+} // extern "C"
+
+namespace {
+
+// pgemm_run_ld, and with `noalloc` pgemm_run_noalloc: the stream-K workspace is then the
+// device's `scratch` array (at most PGEMM_NOALLOC_SCRATCH_BYTES) instead of the handle's.
+int run_impl(pgemm_handle_t h, const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+             int64_t M, int64_t N, int64_t K, int dtype, int sched_mode, int grid_multiple, bool noalloc) {
   int rc = check_common(h, M, N, K, dtype, sched_mode);
   if (rc != PGEMM_OK) return rc;
   h->last_error[0] = 0;
@@ -370,7 +435,15 @@ int pgemm_run_ld(pgemm_handle_t h, const void* A, int64_t lda, const void* B, in
   p.sk_tiles = pl.sk_tiles;
   p.sk_groups = pl.sk_groups;
   p.work = nullptr;
-  if (pl.work_bytes) {
+  if (pl.work_bytes && noalloc) {
+    if (pl.work_bytes > PGEMM_NOALLOC_SCRATCH_BYTES)
+      return fail(h, PGEMM_ERR_UNSUPPORTED,
+                  "stream-K split needs %zu bytes of partial tiles, more than the %zu-byte device scratch of "
+                  "pgemm_run_noalloc (use pgemm_run)",
+                  pl.work_bytes, (size_t)PGEMM_NOALLOC_SCRATCH_BYTES);
+    p.work = scratch_of(h->device);
+    if (!p.work) return fail(h, PGEMM_ERR_HIP, "device scratch of device %d was not set up", h->device);
+  } else if (pl.work_bytes) {
     if (pl.work_bytes > h->work_bytes) {
       // grow the workspace: wait for launches that may still use the old one
       if (hipStreamSynchronize(h->stream) != hipSuccess) return fail(h, PGEMM_ERR_HIP, "stream synchronize failed");
@@ -431,6 +504,10 @@ int pgemm_run_ld(pgemm_handle_t h, const void* A, int64_t lda, const void* B, in
   }
   return PGEMM_OK;
 }
+
+} // namespace
+
+extern "C" {
 
 int pgemm_destroy(pgemm_handle_t h) {
   if (!h) return PGEMM_OK;
