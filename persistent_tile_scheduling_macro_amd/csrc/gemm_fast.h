@@ -378,7 +378,7 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, Tile<CFG>::MIN_WAVES_PE
     if constexpr (SK) {
       if (p_kt == p_ke) {
         p_tile = next_unit(p_walk, &p_kt, &p_ke);
-        if (p_tile >= T) {
+        if ((unsigned)p_tile >= (unsigned)T) {
           p_done = true;
           return;
         }
@@ -389,7 +389,9 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, Tile<CFG>::MIN_WAVES_PE
       kt = issued - q * nk;
       if (kt == 0) {
         p_tile = tile_of(q);
-        if (p_tile >= T) {
+        // any id outside [0, T) ends the sequence (a ring entry is only ever a tile id or
+        // T; the unsigned compare keeps even a corrupt negative value off the tile grid)
+        if ((unsigned)p_tile >= (unsigned)T) {
           p_done = true;
           return;
         }
@@ -682,7 +684,7 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, Tile<CFG>::MIN_WAVES_PE
     __syncthreads();
     if constexpr (SCHED == kCancel) {
       // a workgroup that found no tile left exits here, all of it at once
-      if (tile_of(0) >= T) return;
+      if ((unsigned)tile_of(0) >= (unsigned)T) return;
     }
   }
   int c_kb = 0, c_ke = nk; // k-step range of the consumer's unit
@@ -731,6 +733,9 @@ __global__ void __launch_bounds__(Tile<CFG>::WAVES * 64, Tile<CFG>::MIN_WAVES_PE
     }
     if (!has_next) break;
     if constexpr (SK) c_tile = next_unit(c_walk, &c_kb, &c_ke); else c_tile = tile_of(++c_q);
+    // the producer resolved the same published entry and began this tile only if it lies in
+    // [0, T); the consumer checks it too, so the two can never disagree on a corrupt entry
+    if ((unsigned)c_tile >= (unsigned)T) break;
   }
 }
 

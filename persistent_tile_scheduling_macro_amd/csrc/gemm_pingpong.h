@@ -150,7 +150,7 @@ __global__ void __launch_bounds__(512, 2) gemm_pp_kernel(Params p) {
     }
     __syncthreads();
     if constexpr (SCHED == kCancel) {
-      if (tile_of(0) >= T) return; // found no tile: the whole workgroup leaves at once
+      if ((unsigned)tile_of(0) >= (unsigned)T) return; // found no tile: the whole workgroup leaves at once
     }
   }
 
@@ -227,7 +227,7 @@ __global__ void __launch_bounds__(512, 2) gemm_pp_kernel(Params p) {
     if (u_done) return;
     if (u_kt == 0) {
       const int t = tile_of(u_q);
-      if (t >= T) {
+      if ((unsigned)t >= (unsigned)T) { // any id outside [0, T) ends the sequence
         u_done = true;
         return;
       }
@@ -464,7 +464,7 @@ __global__ void __launch_bounds__(512, 2) gemm_pp_kernel(Params p) {
         step(I0{});
         step(I1{});
       }
-      if (tile_of(q + 1) >= T) break;
+      if ((unsigned)tile_of(q + 1) >= (unsigned)T) break;
       epilogue(grp_c, tile_of(q));
       zero_acc();
       ++q;
