@@ -121,8 +121,8 @@ def parse():
                          "nk = N x K row-major (B transposed, as a linear layer stores its weight)")
     ap.add_argument("--tile", default="auto", choices=["auto", "256", "128"],
                     help="macro tile of the fast kernel (auto: the library's default choice)")
-    ap.add_argument("--mainloop", default="auto", choices=["auto", "lockstep", "pingpong"],
-                    help="wave schedule of the 256 x 256 tile (auto: the library's default choice)")
+    ap.add_argument("--mainloop", default="auto", choices=["auto", "lockstep", "pingpong", "producer"],
+                    help="wave schedule of the 256-row tile (auto: the library's default choice; producer: copy waves and MFMA waves, 256 x 128 tiles)")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the summary of the other configured workloads after the timed one")
     ap.add_argument("--small-k-max", type=int, default=None,
@@ -224,6 +224,8 @@ def kernel_name(dtype, mode, info):
     """Name of the kernel that computes a launch's whole tiles (the key of the traffic profiles)."""
     if not info["fast_path"]:
         return f"gemm_generic_kernel<{DT_NAMES[dtype]}, {SCHED_NAMES[mode]}>"
+    if info.get("body") == 3:  # producer waves (never stream-K)
+        return f"gemm_pw_kernel<{DT_NAMES[dtype]}, {SCHED_NAMES[mode]}>"
     if info.get("body") == 2:  # ping-pong; stream-K's whole waves run in its static kernel
         return f"gemm_pp_kernel<{DT_NAMES[dtype]}, {SCHED_NAMES[1 if mode == 4 else mode]}>"
     return f"gemm_fast_kernel<{DT_NAMES[dtype]}, {SCHED_NAMES[mode]}, kTile{info['bm']}>"
@@ -265,7 +267,7 @@ def setup(pg, torch, si, args, workload, tile=None):
     pg.pgemm_set_tile_config(h, {"auto": pg.PGEMM_TILE_AUTO, "256": pg.PGEMM_TILE_256,
                                  "128": pg.PGEMM_TILE_128}[tile])
     pg.pgemm_set_mainloop(h, {"auto": pg.PGEMM_MAINLOOP_AUTO, "lockstep": pg.PGEMM_MAINLOOP_LOCKSTEP,
-                              "pingpong": pg.PGEMM_MAINLOOP_PINGPONG}[args.mainloop])
+                              "pingpong": pg.PGEMM_MAINLOOP_PINGPONG, "producer": pg.PGEMM_MAINLOOP_PRODUCER}[args.mainloop])
     pg.pgemm_set_b_layout(h, pg.PGEMM_B_NK if args.b_layout == "nk" else pg.PGEMM_B_KN)
 
     def launch(p):

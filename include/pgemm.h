@@ -121,8 +121,8 @@ typedef enum {
   PGEMM_TILE_128 = 2
 } pgemm_tile_t;
 
-/* Wave schedule of the 256 x 256 fast tile (pgemm_set_mainloop). The value
- * of C does not depend on it: both schedules give every accumulator the same
+/* Wave schedule of the 256-row fast tile (pgemm_set_mainloop). The value of
+ * C does not depend on it: every schedule gives every accumulator the same
  * MFMAs on the same operands in the same order, so C is bitwise the same.
  * LOCKSTEP: all eight waves of a workgroup copy, read and multiply in step,
  *   one barrier per k-step; each step's global -> LDS copy is issued right
@@ -134,16 +134,25 @@ typedef enum {
  *   alternates between the waves instead of being given to a producer wave,
  *   KernelWiki "Persistent Kernels with Cluster Launch Control", tutorial
  *   note on warp specialization).
+ * PRODUCER: a dedicated load role (the KernelWiki page's producer-side
+ *   request pipeline and its warp-specialization note): waves 4-7 of the
+ *   workgroup only copy operand tiles into a three-stage LDS ring and make
+ *   the tile claims of the claiming modes, waves 0-3 only read fragments and
+ *   run MFMAs. Every wave of a workgroup gets the same register budget on
+ *   CDNA, so with four waves copying the tile shrinks to 256 x 128 (T is
+ *   counted in those tiles). STREAMK keeps the lockstep 256 x 256 body.
+ *   Offered for measurement; AUTO never picks it (measured slower).
  * AUTO (default): PINGPONG for tiles of at least 20 k-steps of 64 for
  *   fp16/bf16 (K >= 1217) and 8 k-steps of 128 for fp8 (K >= 897), LOCKSTEP
  *   below, where its cheaper tile prologue and epilogue win (measured).
  *   The 128 x 128 tile, the generic body and the split tail of STREAMK
- *   always run lockstep. The environment variable PGEMM_MAINLOOP (1 or 2)
+ *   always run lockstep. The environment variable PGEMM_MAINLOOP (1, 2 or 3)
  *   overrides the default at pgemm_create. */
 typedef enum {
   PGEMM_MAINLOOP_AUTO = 0,
   PGEMM_MAINLOOP_LOCKSTEP = 1,
-  PGEMM_MAINLOOP_PINGPONG = 2
+  PGEMM_MAINLOOP_PINGPONG = 2,
+  PGEMM_MAINLOOP_PRODUCER = 3
 } pgemm_mainloop_t;
 
 /* Storage of B (pgemm_set_b_layout). The value of C does not depend on it:
@@ -310,8 +319,9 @@ int pgemm_clock_khz(int device, int* khz);
  * tile count, grid size, occupancy (workgroups per CU), macro tile
  * (bm x bn, k-step bk in elements), and the tile body of the launch that
  * computes the whole tiles: 0 = the generic kernel (unaligned sizes),
- * 1 = the fast kernel with lockstep waves, 2 = the fast kernel in ping-pong
- * (pgemm_mainloop_t). Output pointers may be NULL. Alignment is judged from
+ * 1 = the fast kernel with lockstep waves, 2 = the fast kernel in ping-pong,
+ * 3 = the fast kernel with producer waves (pgemm_mainloop_t). Output
+ * pointers may be NULL. Alignment is judged from
  * the sizes only (pointers assumed 16-byte aligned). */
 int pgemm_query_launch(pgemm_handle_t h, int64_t M, int64_t N, int64_t K, int dtype, int sched_mode,
                        int grid_multiple, int* tiles, int* grid, int* occupancy, int* bm, int* bn, int* bk,
@@ -352,7 +362,7 @@ int pgemm_set_tile_config(pgemm_handle_t h, int tile);
  * non-finite scale or a non-finite product. */
 int pgemm_set_fp8_scales(pgemm_handle_t h, float scale_a, float scale_b);
 
-/* Choose the wave schedule of the 256 x 256 tile for later runs on this
+/* Choose the wave schedule of the 256-row tile for later runs on this
  * handle (pgemm_mainloop_t; C's bits do not depend on it). Returns
  * PGEMM_ERR_INVALID_ARG for a NULL handle or an unknown value. */
 int pgemm_set_mainloop(pgemm_handle_t h, int mainloop);

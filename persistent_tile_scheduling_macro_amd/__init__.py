@@ -41,6 +41,7 @@ PGEMM_B_NK = 1
 PGEMM_MAINLOOP_AUTO = 0
 PGEMM_MAINLOOP_LOCKSTEP = 1
 PGEMM_MAINLOOP_PINGPONG = 2
+PGEMM_MAINLOOP_PRODUCER = 3
 
 DTYPE_NAMES = {"f16": PGEMM_F16, "bf16": PGEMM_BF16, "e4m3fn": PGEMM_F8E4M3_BF16}
 SCHED_NAMES = {"nonpersistent": PGEMM_SCHED_NONPERSISTENT, "static": PGEMM_SCHED_STATIC,
@@ -202,7 +203,7 @@ def pgemm_query_launch(h, M: int, N: int, K: int, dtype: int, sched_mode: int, g
                          *[ctypes.byref(o) for o in out]), h)
     keys = ["tiles", "grid", "occupancy", "bm", "bn", "bk", "body"]
     d = {k: o.value for k, o in zip(keys, out)}
-    d["fast_path"] = int(d["body"] != 0)  # 0: generic kernel; body 1 lockstep, 2 ping-pong
+    d["fast_path"] = int(d["body"] != 0)  # 0: generic kernel; body 1 lockstep, 2 ping-pong, 3 producer waves
     return d
 
 
@@ -231,7 +232,7 @@ def pgemm_set_tile_config(h, tile: int) -> None:
 
 
 def pgemm_set_mainloop(h, mainloop: int) -> None:
-    """Wave schedule of the 256 x 256 tile: PGEMM_MAINLOOP_AUTO, _LOCKSTEP or _PINGPONG."""
+    """Wave schedule of the 256-row tile: PGEMM_MAINLOOP_AUTO, _LOCKSTEP, _PINGPONG or _PRODUCER."""
     _check(_set_mainloop(h, int(mainloop)), h)
 
 

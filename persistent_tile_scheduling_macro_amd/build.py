@@ -25,7 +25,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpgemm.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = ["pgemm.hip", "kernels_f16.hip", "kernels_bf16.hip", "kernels_f8.hip", "kernels_pp_f16.hip",
-           "kernels_pp_bf16.hip", "kernels_pp_f8.hip", "hold.hip"]
+           "kernels_pp_bf16.hip", "kernels_pp_f8.hip", "kernels_pw_f16.hip", "kernels_pw_bf16.hip", "kernels_pw_f8.hip",
+           "hold.hip"]
 ARCH = os.environ.get("PGEMM_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -9,10 +9,11 @@ typedef void (*kernel_fn)(Params);
 
 // Tile body of a launch: the fast kernel in one of its two macro-tile
 // configurations (lockstep waves), the 256 x 256 ping-pong form of the fast
-// kernel (gemm_pingpong.h), or the generic 64 x 64 body for unaligned
+// kernel (gemm_pingpong.h), the 256 x 128 producer-wave form (copy waves and
+// MFMA waves, gemm_producer.h), or the generic 64 x 64 body for unaligned
 // operands.
-enum Body : int { kBodyGeneric = 0, kBodyTile256 = 1, kBodyTile128 = 2, kBodyPingPong = 3 };
-constexpr int kNumBodies = 4;
+enum Body : int { kBodyGeneric = 0, kBodyTile256 = 1, kBodyTile128 = 2, kBodyPingPong = 3, kBodyProducer = 4 };
+constexpr int kNumBodies = 5;
 
 // Returns the kernel for (scheduling mode, tile body); `trace` selects the
 // fast bodies' instantiation that writes the tile trace, `bt` the one that
@@ -27,6 +28,12 @@ kernel_fn pick_kernel_f8(int sched, int body, bool trace, bool bt);
 kernel_fn pick_kernel_pp_f16(int sched, bool trace, bool bt);
 kernel_fn pick_kernel_pp_bf16(int sched, bool trace, bool bt);
 kernel_fn pick_kernel_pp_f8(int sched, bool trace, bool bt);
+
+// The producer-wave 256 x 128 kernel for the same four modes (kernels_pw_*.hip);
+// nullptr for stream-K, which that body does not serve.
+kernel_fn pick_kernel_pw_f16(int sched, bool trace, bool bt);
+kernel_fn pick_kernel_pw_bf16(int sched, bool trace, bool bt);
+kernel_fn pick_kernel_pw_f8(int sched, bool trace, bool bt);
 
 // The stream-K fix-up kernel of a fast tile body (nullptr for the generic body).
 kernel_fn pick_fixup_f16(int body);

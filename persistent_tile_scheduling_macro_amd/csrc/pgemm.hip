@@ -42,7 +42,7 @@ struct pgemm_ctx {
   int group_m = 4;
   int xcd_remap = -1;
   int tile = PGEMM_TILE_AUTO; // macro-tile choice of the fast kernel
-  int mainloop = PGEMM_MAINLOOP_AUTO; // lockstep or ping-pong waves for the 256 x 256 tile
+  int mainloop = PGEMM_MAINLOOP_AUTO; // lockstep, ping-pong or producer waves for the 256-row tile
   // Stream-K: shortest piece, in k-step pairs, a split may cut (tiles with
   // fewer pairs are not split).
   int sk_min_pairs = 4;
@@ -109,6 +109,7 @@ BodyShape body_shape(int body) {
   switch (body) {
     case kBodyTile256:
     case kBodyPingPong: return {256, 256, 512};
+    case kBodyProducer: return {256, 128, 512};
     case kBodyTile128: return {128, 128, 256};
     default: return {64, 64, 256};
   }
@@ -123,6 +124,13 @@ kernel_fn pick_kernel(int dtype, int sched, int body, bool trace = false, bool b
       case kF16: return pick_kernel_pp_f16(sched, trace, bt);
       case kBF16: return pick_kernel_pp_bf16(sched, trace, bt);
       default: return pick_kernel_pp_f8(sched, trace, bt);
+    }
+  }
+  if (body == kBodyProducer) {
+    switch (dtype) {
+      case kF16: return pick_kernel_pw_f16(sched, trace, bt);
+      case kBF16: return pick_kernel_pw_bf16(sched, trace, bt);
+      default: return pick_kernel_pw_f8(sched, trace, bt);
     }
   }
   switch (dtype) {
@@ -155,7 +163,7 @@ kernel_fn pick_fixup(int dtype, int body) {
 constexpr int kPingPongMinSteps16 = 20; // fp16 / bf16: K >= 1217
 constexpr int kPingPongMinSteps8 = 8;   // e4m3: K >= 897
 
-int choose_body(const pgemm_ctx* h, int64_t M, int64_t N, int64_t K, int dtype, bool fast) {
+int choose_body(const pgemm_ctx* h, int64_t M, int64_t N, int64_t K, int dtype, int sched, bool fast) {
   if (!fast) return kBodyGeneric;
   int body;
   if (h->tile == PGEMM_TILE_256) {
@@ -168,6 +176,9 @@ int choose_body(const pgemm_ctx* h, int64_t M, int64_t N, int64_t K, int dtype, 
   }
   if (body != kBodyTile256 || h->mainloop == PGEMM_MAINLOOP_LOCKSTEP) return body;
   if (h->mainloop == PGEMM_MAINLOOP_PINGPONG) return kBodyPingPong;
+  // the producer-wave body takes the place of the 256 x 256 tile in the tile-sequence
+  // modes; stream-K keeps the lockstep 256 x 256 body (its tail kernel and fix-up)
+  if (h->mainloop == PGEMM_MAINLOOP_PRODUCER) return sched == kStreamK ? kBodyTile256 : kBodyProducer;
   const int64_t bk = dtype == kF8E4M3 ? 128 : 64;
   const int64_t nk = ((K + bk - 1) / bk + 1) & ~(int64_t)1;
   return nk >= (dtype == kF8E4M3 ? kPingPongMinSteps8 : kPingPongMinSteps16) ? kBodyPingPong : kBodyTile256;
@@ -227,7 +238,7 @@ void plan_streamk(const pgemm_ctx* h, int64_t K, int64_t G_full, Plan* pl) {
 int plan_launch(pgemm_ctx* h, int64_t M, int64_t N, int64_t K, int dtype, int sched, int grid_multiple,
                 bool fast, Plan* pl) {
   pl->fast = fast;
-  pl->body = choose_body(h, M, N, K, dtype, fast);
+  pl->body = choose_body(h, M, N, K, dtype, sched, fast);
   const BodyShape bs = body_shape(pl->body);
   pl->threads = bs.threads;
   pl->bm = bs.bm;
@@ -333,7 +344,9 @@ int pgemm_create(pgemm_handle_t* out, int device) {
   }
   if (const char* m = getenv("PGEMM_MAINLOOP")) {
     const int v = atoi(m);
-    h->mainloop = v == PGEMM_MAINLOOP_LOCKSTEP || v == PGEMM_MAINLOOP_PINGPONG ? v : PGEMM_MAINLOOP_AUTO;
+    h->mainloop = v == PGEMM_MAINLOOP_LOCKSTEP || v == PGEMM_MAINLOOP_PINGPONG || v == PGEMM_MAINLOOP_PRODUCER
+                      ? v
+                      : PGEMM_MAINLOOP_AUTO;
   }
   *out = h;
   return PGEMM_OK;
@@ -614,8 +627,9 @@ int pgemm_query_launch(pgemm_handle_t h, int64_t M, int64_t N, int64_t K, int dt
   if (bn) *bn = pl.bn;
   if (bk) *bk = pl.bk;
   if (body) {
-    // the tile body of the launch that does the GEMM's whole tiles: 0 generic, 1 lockstep, 2 ping-pong
-    *body = !pl.fast ? 0 : pl.body == kBodyPingPong ? 2 : 1;
+    // the tile body of the launch that does the GEMM's whole tiles: 0 generic, 1 lockstep,
+    // 2 ping-pong, 3 producer waves
+    *body = !pl.fast ? 0 : pl.body == kBodyPingPong ? 2 : pl.body == kBodyProducer ? 3 : 1;
   }
   return PGEMM_OK;
 }
@@ -654,7 +668,7 @@ int pgemm_set_tile_config(pgemm_handle_t h, int tile) {
 
 int pgemm_set_mainloop(pgemm_handle_t h, int mainloop) {
   if (!h) return PGEMM_ERR_INVALID_ARG;
-  if (mainloop < PGEMM_MAINLOOP_AUTO || mainloop > PGEMM_MAINLOOP_PINGPONG)
+  if (mainloop < PGEMM_MAINLOOP_AUTO || mainloop > PGEMM_MAINLOOP_PRODUCER)
     return fail(h, PGEMM_ERR_INVALID_ARG, "unknown mainloop %d", mainloop);
   h->mainloop = mainloop;
   return PGEMM_OK;

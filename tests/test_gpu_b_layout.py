@@ -22,8 +22,9 @@ pytestmark = pytest.mark.gpu
 DT = {"f16": 0, "bf16": 1, "e4m3fn": 2}
 OUT = {"f16": ("f16", torch.float16), "bf16": ("bf16", torch.bfloat16), "e4m3fn": ("bf16", torch.bfloat16)}
 TOL = {"f16": 2e-3, "bf16": 2e-3, "e4m3fn": 1e-2}
-# (tile config, mainloop): the 256 x 256 tile with lockstep waves and in ping-pong, and 128 x 128
-TILES = {"t256_lockstep": (1, 1), "t256_pingpong": (1, 2), "t128": (2, 0)}
+# (tile config, mainloop): the 256 x 256 tile with lockstep waves and in ping-pong, the 256 x 128
+# tile of the producer-wave body (stream-K keeps the lockstep 256 x 256 body), and 128 x 128
+TILES = {"t256_lockstep": (1, 1), "t256_pingpong": (1, 2), "t256x128_producer": (1, 3), "t128": (2, 0)}
 
 
 @pytest.fixture(scope="module")

@@ -20,8 +20,9 @@ import seeded_inputs as si
 
 pytestmark = pytest.mark.gpu
 
-# (tile config, mainloop): the 256 x 256 tile with lockstep waves and in ping-pong, and 128 x 128
-TILES = {"t256_lockstep": (1, 1), "t256_pingpong": (1, 2), "t128": (2, 0)}
+# (tile config, mainloop): the 256 x 256 tile with lockstep waves and in ping-pong, the 256 x 128
+# tile of the producer-wave body (stream-K keeps the lockstep 256 x 256 body), and 128 x 128
+TILES = {"t256_lockstep": (1, 1), "t256_pingpong": (1, 2), "t256x128_producer": (1, 3), "t128": (2, 0)}
 F8 = 2
 
 

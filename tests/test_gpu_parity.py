@@ -28,8 +28,9 @@ OUT = {"f16": ("f16", torch.float16), "bf16": ("bf16", torch.bfloat16), "e4m3fn"
 TOL = {"f16": 2e-3, "bf16": 2e-3, "e4m3fn": 1e-2}
 MODES = [0, 1, 2, 3, 4]  # non-persistent, static, dynamic, cancel-and-reuse, stream-K
 SAME_BITS = [0, 1, 2, 3]  # modes that run every tile whole: C bitwise identical
-# (tile config, mainloop): the 256 x 256 tile with lockstep waves and in ping-pong, and 128 x 128
-TILES = {"t256_lockstep": (1, 1), "t256_pingpong": (1, 2), "t128": (2, 0)}
+# (tile config, mainloop): the 256 x 256 tile with lockstep waves and in ping-pong, the 256 x 128
+# tile of the producer-wave body (stream-K keeps the lockstep 256 x 256 body), and 128 x 128
+TILES = {"t256_lockstep": (1, 1), "t256_pingpong": (1, 2), "t256x128_producer": (1, 3), "t128": (2, 0)}
 
 
 @pytest.fixture(scope="module")
@@ -84,7 +85,7 @@ def test_workload_256_all_modes(pg, handle, dtype):
         c, v, info = run(pg, handle, A, B, dtype, mode)
         err = oracle.normwise_error(c, OUT[dtype][0], ref)
         assert err <= TOL[dtype], (mode, err)
-        assert info["fast_path"] == 1 and info["tiles"] == (256 // info["bm"]) ** 2
+        assert info["fast_path"] == 1 and info["tiles"] == (256 // info["bm"]) * (256 // info["bn"])
         assert np.array_equal(v, np.ones_like(v)), v
         if mode in SAME_BITS:
             outs.append(c)
@@ -285,6 +286,28 @@ def test_modes_while_cus_are_held(pg, handle):
         assert bool(torch.all(visits == 1)), mode
         assert np.array_equal(si.bits(C.cpu()), want), mode
         assert pg.pgemm_read_work_counter(handle) == 0
+
+
+def test_producer_wave_body_launch_report(pg):
+    """The producer-wave mainloop runs the 256 x 128 tile body (body 3) in the four
+    tile-sequence modes, at every size the fast kernel takes, and leaves stream-K on the
+    lockstep 256 x 256 body (body 1), with the 256-row tile chosen."""
+    h = pg.pgemm_create(0)
+    try:
+        pg.pgemm_set_tile_config(h, pg.PGEMM_TILE_256)
+        pg.pgemm_set_mainloop(h, pg.PGEMM_MAINLOOP_PRODUCER)
+        for dcode in (0, 1, 2):
+            for (M, N, K) in [(256, 256, 64), (8192, 8192, 8192), (1000, 1040, 528)]:  # fast-kernel sizes for every dtype
+                for mode in (0, 1, 2, 3):
+                    info = pg.pgemm_query_launch(h, M, N, K, dcode, mode, 0)
+                    assert (info["body"], info["bm"], info["bn"]) == (3, 256, 128), (dcode, M, mode, info)
+                    assert info["tiles"] == -(-M // 256) * -(-N // 128)
+                info = pg.pgemm_query_launch(h, M, N, K, dcode, 4, 0)
+                assert (info["body"], info["bm"], info["bn"]) == (1, 256, 256), (dcode, M, info)
+        with pytest.raises(pg.PgemmError):
+            pg.pgemm_set_mainloop(h, 4)
+    finally:
+        pg.pgemm_destroy(h)
 
 
 def test_graph_capture_and_replay(pg):

@@ -18,7 +18,10 @@ the three tile bodies:
   begun after it;
 * ping-pong: waves 0-3 (X) and 4-7 (Y) in opposite phases, two barriers per
   step, each group beginning its copy of step s + 1 in its memory phase of
-  step s; claims finished at the end of X's compute phase.
+  step s; claims finished at the end of X's compute phase;
+* producer waves: copy waves (which also claim) and MFMA waves meet at one
+  barrier per step; the copy waves begin step j + 2 after barrier j, and
+  both roles must pass the same number of barriers.
 
 It checks the shipped protocols for every k-loop length and tile count, and
 it characterizes the variant dropped during development, which published the
@@ -194,6 +197,76 @@ def pingpong(mode, nk, ntiles):
     return t
 
 
+def producer(mode, nk, ntiles):
+    """Producer-wave body. Barrier numbering as in the other models: the claims barrier, then
+    barrier 0 (step 0 has landed), then barrier j + 1 for every step j that has a successor.
+    Copy waves: steps 0 and 1 are copied before barrier 0, step j + 2 after barrier j; a tile's
+    first copy reads its ring entry; the claim for tile q + 1 is issued with the copy of tile q's
+    step 1 (step 3 for cancel-and-reuse's tile 0 when nk >= 4) and written to the ring before the
+    next barrier. MFMA waves: at the last step of tile q they read entry q + 1 to learn whether a
+    step follows; the epilogue reads entry q. Returns the trace and the barrier counts of the two
+    roles."""
+    t = Trace()
+    S = ntiles * nk
+    defer = mode == "cancel" and nk >= 4
+
+    def cstep(q):
+        return 3 if (defer and q == 0) else 1
+
+    # ---- copy waves
+    t.write(0)          # both claiming modes keep their first tile in the ring
+    t.barrier()         # claims barrier
+    if mode == "cancel":
+        t.read(0, "exit check")
+    pending = []
+    issued = [0]
+
+    def issue(u):
+        if u >= S:
+            return False
+        q, kt = divmod(u, nk)
+        if kt == 0:
+            t.read(q, "copy waves")
+        if kt == cstep(q):
+            pending.append(q + 1)   # the claim of tile q + 1 (tile ntiles: the failing one)
+        issued[0] += 1
+        return True
+
+    def publish():
+        while pending:
+            t.write(pending.pop())
+
+    issue(0)
+    issue(1)
+    publish()
+    t.barrier()         # barrier 0
+    j = 0
+    while True:
+        issue(j + 2)
+        if j + 1 >= issued[0]:
+            break
+        publish()
+        t.barrier()     # barrier j + 1
+        j += 1
+    copy_barriers = t.barriers
+    # ---- MFMA waves (the same barriers, counted from the claims barrier)
+    b = 1
+    if mode == "cancel":
+        t.reads.append((0, b, "exit check (MFMA waves)"))
+    b += 1              # barrier 0
+    for s in range(S):
+        q, kt = divmod(s, nk)
+        nxt = True
+        if kt == nk - 1:
+            t.reads.append((q + 1, b, "MFMA waves: next"))
+            nxt = q + 1 < ntiles
+        if nxt:
+            b += 1
+        if kt == nk - 1:
+            t.reads.append((q, b, "MFMA waves: epilogue"))
+    return t, copy_barriers, b
+
+
 NKS = [2, 4, 6, 8, 16, 64]
 BODIES = {"lockstep16": lockstep16, "lockstep8": lockstep8, "pingpong": pingpong}
 
@@ -250,3 +323,18 @@ def test_dropped_variant_races_exactly_at_short_k_loops(body):
         vals = [first_safe[(p, after)] for p in range(6)]
         vals = [v if v is not None else 10**9 for v in vals]
         assert vals == sorted(vals)
+
+
+@pytest.mark.parametrize("mode", ["dynamic", "cancel"])
+def test_producer_body_roles_pass_the_same_barriers_and_publish_before_reading(mode):
+    """The copy waves and the MFMA waves of the producer-wave body must meet at exactly the same
+    barriers (a mismatch would leave one role waiting forever), and every ring entry must be
+    published before any wave reads it: for every even k-loop length and tile count."""
+    for nk, ntiles in itertools.product([2, 4, 6, 8, 10, 16, 64], [1, 2, 3, 5, 9]):
+        t, copy_b, mfma_b = producer(mode, nk, ntiles)
+        assert copy_b == mfma_b == 1 + ntiles * nk, (mode, nk, ntiles, copy_b, mfma_b)
+        assert t.races() == [], (mode, nk, ntiles, t.races())
+        needed = {q for q, _, _ in t.reads}
+        assert needed <= set(t.writes), (mode, nk, ntiles, needed - set(t.writes))
+        # one claim per tile, the last of them the failing one (entry ntiles)
+        assert sorted(t.writes) == list(range(ntiles + 1)), (mode, nk, ntiles)
