@@ -749,17 +749,21 @@ def run_uneven(args, pg, si, torch, np):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e-3
 
-    # The clock sags over a burst of 8192^3 launches (power limit), so a fixed order
-    # would favour whichever mode runs first: the order rotates every step.
+    # The clock sags over a burst of 8192^3 launches (power limit: a launch late in a
+    # step's burst measured up to 30% slower than the first), so a fixed order would
+    # favour whichever mode runs first: the order rotates every step, and the step count
+    # is rounded up to whole rotations so that every mode takes every position equally
+    # often.
     def order(s):
         r = s % len(modes)
         return modes[r:] + modes[:r]
 
+    steps = -(-args.steps // len(modes)) * len(modes)
     for s in range(args.warmup):
         for hc in held_set:
             for m in order(s):
                 one(hc, m)
-    for s in range(args.steps):
+    for s in range(steps):
         for hc in held_set:
             for m in order(s):
                 times[(hc, m)].append(one(hc, m))
@@ -808,8 +812,8 @@ def run_uneven(args, pg, si, torch, np):
     value = flops * n_runs / tot_t / 1e12
     result = {
         "metric": "GEMM TFLOPS and % of dense MFMA peak vs K; persistent vs non-persistent",
-        "value": round(value, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(tot_t / args.steps * 1e3, 3), "higher_is_better": True, "scaling": "weak",
+        "value": round(value, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": args.warmup,
+        "ms_per_step": round(tot_t / steps * 1e3, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": dtype, "data": "synthetic",
         "config": {"workload": desc, "name": "uneven", "hold_cus": held_set[1], "hold_us": args.hold_us,
                    "cus": cus},
