@@ -115,3 +115,44 @@ def test_workload_sampled_parity(pg, handle, workload):
                     assert torch.equal(cb, first), (mode, gm, "C differs bitwise from the first mode")
             del Ad, Bd, first
             torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("K", [5120, 8192])
+def test_producer_wave_body_at_full_size(pg, K):
+    """The producer-wave body (bench.py --mainloop producer) on the 8192^2 sweep's points in
+    modes 0-3: sampled rows against the oracle, every tile written once, and C bitwise equal
+    to the default body's C (the bodies give every accumulator the same MFMAs in the same
+    order)."""
+    desc, dtype, kind, wid, probs = bench.problems("sweep8k")
+    m = n = 8192
+    dev = torch.device("cuda:0")
+    A, B = si.operands(m, n, 8192, dtype, kind, workload=wid)
+    Ak, Bk = A[:, :K].contiguous(), B[:K, :].contiguous()
+    rows = sample_rows(m, seed=K)
+    ref = oracle.gemm(si.bits(Ak), si.bits(Bk), dtype, rows=rows)
+    Ad, Bd = Ak.to(dev), Bk.to(dev)
+    rows_d = torch.from_numpy(rows).to(dev)
+    h0, h = pg.pgemm_create(0), pg.pgemm_create(0)
+    try:
+        pg.pgemm_set_mainloop(h, pg.PGEMM_MAINLOOP_PRODUCER)
+        want = torch.empty((m, n), dtype=OUT[dtype][1], device=dev)
+        pg.pgemm_run(h0, Ad, Bd, want, m, n, K, DT[dtype], 1, 0)
+        for mode in (0, 1, 2, 3):
+            print(f"case producer body 8192x8192x{K} mode {mode}", flush=True)
+            info = pg.pgemm_query_launch(h, m, n, K, DT[dtype], mode, 0)
+            assert (info["body"], info["bm"], info["bn"]) == (3, 256, 128)
+            visits = torch.zeros(info["tiles"], dtype=torch.int32, device=dev)
+            C = torch.full((m, n), float("nan"), dtype=OUT[dtype][1], device=dev)
+            pg.pgemm_set_tile_counter(h, visits)
+            try:
+                pg.pgemm_run(h, Ad, Bd, C, m, n, K, DT[dtype], mode, 0)
+                torch.cuda.synchronize()
+            finally:
+                pg.pgemm_set_tile_counter(h, None)
+            assert bool(torch.all(visits == 1)), mode
+            err = oracle.normwise_error(si.bits(C.index_select(0, rows_d).cpu()), OUT[dtype][0], ref)
+            assert err <= TOL[dtype], (mode, err)
+            assert torch.equal(C.view(torch.int16), want.view(torch.int16)), mode
+    finally:
+        pg.pgemm_destroy(h)
+        pg.pgemm_destroy(h0)
