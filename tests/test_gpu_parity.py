@@ -310,20 +310,29 @@ def test_producer_wave_body_launch_report(pg):
         pg.pgemm_destroy(h)
 
 
-def test_graph_capture_and_replay(pg):
+# (tile config, mainloop, M, N, K): 48 tiles of 128^2, where stream-K splits each in two (a
+# fix-up node too); and 256-row tiles with a k-loop long enough for the ping-pong body
+# (stream-K: a ping-pong whole-wave launch, a lockstep tail and a fix-up) and the producer body
+GRAPH_CASES = {"t128": (2, 0, 1024, 768, 1024), "t256_pingpong": (1, 2, 1280, 1024, 2048),
+               "t256x128_producer": (1, 3, 1280, 1024, 2048)}
+
+
+@pytest.mark.parametrize("case", sorted(GRAPH_CASES))
+def test_graph_capture_and_replay(pg, case):
     """pgemm_run is capture-safe: no memsets, and the claiming modes' work
     counter resets itself inside the kernel. A HIP graph holding one launch per
     scheduling mode is replayed several times with eager work in between;
     every replay's C is bit-exact and the counter reads 0 after each."""
+    tile, mainloop, M, N, K = GRAPH_CASES[case]
     dev = torch.device("cuda:0")
-    M, N, K = 1024, 768, 1024  # 48 tiles of 128^2: stream-K splits each in two (a fix-up node too)
     A, B = si.operands(M, N, K, "f16", "small_int", workload=13)
     want = oracle.round_to(oracle.gemm(si.bits(A), si.bits(B), "f16"), "f16")
     Ad, Bd = A.to(dev), B.to(dev)
     Cs = [torch.empty((M, N), dtype=torch.float16, device=dev) for _ in MODES]
     h = pg.pgemm_create(0)
     try:
-        pg.pgemm_set_tile_config(h, pg.PGEMM_TILE_128)
+        pg.pgemm_set_tile_config(h, tile)
+        pg.pgemm_set_mainloop(h, mainloop)
         for C, mode in zip(Cs, MODES):  # eager runs first: any stream-K workspace exists before capture
             pg.pgemm_run(h, Ad, Bd, C, M, N, K, 0, mode, 0)
         torch.cuda.synchronize()
