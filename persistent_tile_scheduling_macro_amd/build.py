@@ -58,7 +58,7 @@ def parse_resource_remarks(text: str) -> list:
 
 def is_traced(name: str) -> bool:
     """Tile-trace instantiation of a fast kernel: its first bool template argument (TRACE) is true."""
-    m = re.search(r"(gemm_fast_kernel|gemm_pp_kernel)I(?:Li\d+E)+Lb(\d)E", name)
+    m = re.search(r"(gemm_fast_kernel|gemm_pp_kernel|gemm_pw_kernel)I(?:Li\d+E)+Lb(\d)E", name)
     return bool(m and m.group(2) == "1")
 
 

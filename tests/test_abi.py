@@ -155,6 +155,24 @@ def test_b_layout_argument_checks(pg):
         assert m and int(m.group(1)) == getattr(pg, name)
 
 
+def test_mainloop_argument_checks(pg):
+    """The wave-schedule setter needs a handle; the schedule constants match the header, and the
+    library was built with the producer-wave kernels (the body only the setter selects)."""
+    with pytest.raises(pg.PgemmError) as e:
+        pg.pgemm_set_mainloop(None, pg.PGEMM_MAINLOOP_PRODUCER)
+    assert e.value.status == pg.PGEMM_ERR_INVALID_ARG
+    text = open(HEADER).read()
+    for name, val in (("PGEMM_MAINLOOP_AUTO", 0), ("PGEMM_MAINLOOP_LOCKSTEP", 1), ("PGEMM_MAINLOOP_PINGPONG", 2),
+                      ("PGEMM_MAINLOOP_PRODUCER", 3)):
+        m = re.search(name + r"\s*=\s*(\d+)", text)
+        assert m and int(m.group(1)) == getattr(pg, name) == val
+    path = os.path.join(ROOT, "persistent_tile_scheduling_macro_amd", "_build", "kernel_resources.txt")
+    if os.path.exists(path):
+        names = {l.split()[0] for l in open(path) if not l.startswith("#")}
+        for body in ("gemm_pp_kernel", "gemm_pw_kernel"):
+            assert sum(body in n for n in names) == 48, body  # 3 dtypes x 4 modes x traced x B layout
+
+
 def test_fp8_scales_argument_checks(pg):
     """The fp8 scale setter needs a handle (no device is touched on the failure path)."""
     with pytest.raises(pg.PgemmError) as e:
@@ -189,6 +207,10 @@ def test_resource_remark_parser_and_trace_flag():
     assert ks[1]["scratch"] == 12
     assert not b.is_traced(ks[0]["name"]) and b.is_traced(ks[1]["name"])
     assert not b.is_traced("_ZN5pgemm7generic19gemm_generic_kernelILi0ELi1EEEvNS_6ParamsE")
+    # the ping-pong and producer-wave bodies' traced instantiations (TRACE is their first bool)
+    assert b.is_traced("_ZN5pgemm2pp14gemm_pp_kernelILi0ELi1ELb1ELb0EEEvNS_6ParamsE")
+    assert b.is_traced("_ZN5pgemm2pw14gemm_pw_kernelILi2ELi3ELb1ELb1EEEvNS_6ParamsE")
+    assert not b.is_traced("_ZN5pgemm2pw14gemm_pw_kernelILi2ELi3ELb0ELb1EEEvNS_6ParamsE")
 
 
 def test_built_kernels_do_not_spill():
@@ -202,5 +224,5 @@ def test_built_kernels_do_not_spill():
     for name, vgpr, agpr, sgpr, scratch, occ, lds, traced in rows:
         if traced == "0":
             assert int(scratch) == 0, name
-        if "gemm_fast_kernel" in name or "gemm_pp_kernel" in name:
+        if "gemm_fast_kernel" in name or "gemm_pp_kernel" in name or "gemm_pw_kernel" in name:
             assert int(occ) >= 2 and int(vgpr) >= 0, name
