@@ -314,9 +314,20 @@ def small_k_crossover(torch, np, env, k_max, rounds=100):
         env["launch"](p)
     torch.cuda.synchronize()
     times = rotated_launch_times(torch, env["stream"], probs, env["launch"], rounds)
+    out = crossover_summary(times, np)
+    out["launches_per_point"] = rounds
+    return out
+
+
+def crossover_summary(times, np):
+    """The small-K pass's analysis, from {problem: [seconds per launch]}: per K the median, min
+    and max of every variant, the fastest variant, the non-persistent median over the best
+    persistent one and whether their [min, max] ranges are separated; the K values where each
+    side leads; and the crossover K (the smallest K from which non-persistent is at least as
+    fast at every larger measured K; None when persistent leads at the largest)."""
     by_k = {}
-    for p in probs:
-        us = sorted(t * 1e6 for t in times[p])
+    for p, ts in times.items():
+        us = sorted(t * 1e6 for t in ts)
         by_k.setdefault(p[2], {})[variant_name(p)] = {
             "median_us": round(float(np.median(us)), 2), "min_us": round(us[0], 2), "max_us": round(us[-1], 2),
             "tflops_median": round(2.0 * p[0] * p[1] * p[2] / (np.median(us) * 1e-6) / 1e12, 1)}
@@ -343,7 +354,7 @@ def small_k_crossover(torch, np, env, k_max, rounds=100):
         if not np_wins:
             break
         cross = K
-    return {"launches_per_point": rounds, "order": "rotated by one variant per round", "points": points,
+    return {"order": "rotated by one variant per round", "points": points,
             "persistent_ahead_at_K": [K for K, w in ahead if not w],
             "nonpersistent_ahead_at_K": [K for K, w in ahead if w],
             "crossover_K": cross}

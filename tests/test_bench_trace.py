@@ -61,3 +61,49 @@ def test_vendor_flag_parses(monkeypatch):
     assert args.vendor and args.b_layout == "nk"
     monkeypatch.setattr("sys.argv", ["bench.py"])
     assert not bench.parse().vendor
+
+
+def test_crossover_summary_on_hand_made_timings():
+    """Persistent leads at K = 256 (ranges separated), non-persistent from K = 512 on: the
+    crossover is 512; medians, not means, decide (one slow outlier per variant)."""
+    us = 1e-6
+    times = {
+        (8192, 8192, 256, 0, 0): [64 * us] * 99 + [500 * us],
+        (8192, 8192, 256, 1, 1): [54 * us] * 99 + [500 * us],
+        (8192, 8192, 256, 2, 1): [55 * us] * 100,
+        (8192, 8192, 512, 0, 0): [80 * us] * 100,
+        (8192, 8192, 512, 1, 1): [81 * us] * 100,
+        (8192, 8192, 768, 0, 0): [100 * us] * 100,
+        (8192, 8192, 768, 1, 1): [100 * us] * 100,
+    }
+    out = bench.crossover_summary(times, np)
+    p256 = out["points"]["K=256"]
+    assert p256["fastest"] == "static@g1" and p256["best_persistent"] == "static@g1"
+    assert p256["variants"]["nonpersistent"]["median_us"] == 64.0
+    assert p256["variants"]["nonpersistent"]["max_us"] == 500.0
+    assert p256["nonpersistent_over_best_persistent"] == round(64 / 54, 4)
+    assert p256["separated"] is False  # the 500 us outliers overlap the other range
+    assert out["persistent_ahead_at_K"] == [256]
+    assert out["nonpersistent_ahead_at_K"] == [512, 768]  # a tie counts for non-persistent
+    assert out["crossover_K"] == 512
+    # persistent ahead at the largest K: no crossover
+    times[(8192, 8192, 768, 1, 1)] = [90 * us] * 100
+    assert bench.crossover_summary(times, np)["crossover_K"] is None
+
+
+def test_workloads_match_the_configured_problems():
+    """The workload table holds the configured problems: the 256^3 case, the two fp16 K sweeps,
+    fp8 8192^3 and the bf16 tail set, with their modes and grid multiples."""
+    def probs(wl):
+        return bench.problems(wl)[4]
+    assert {(m, n, k) for m, n, k, _, _ in probs("small256")} == {(256, 256, 256)}
+    p4 = probs("sweep4k")
+    assert sorted({k for _, _, k, _, _ in p4}) == list(range(128, 4097, 128))
+    assert {(m, n) for m, n, _, _, _ in p4} == {(4096, 4096)} and {md for _, _, _, md, _ in p4} == {0, 1, 2}
+    p8 = probs("sweep8k")
+    assert sorted({k for _, _, k, _, _ in p8}) == list(range(256, 8193, 256))
+    assert {(md, gm) for _, _, _, md, gm in p8} == {(0, 0), (1, 1), (1, 2), (1, 3), (2, 1), (2, 2), (2, 3)}
+    assert bench.WORKLOADS["fp8"][1] == "e4m3fn" and {(m, n, k) for m, n, k, _, _ in probs("fp8")} == {(8192,) * 3}
+    assert bench.WORKLOADS["tail"][1] == "bf16" and bench.WORKLOADS["tail"][7] == "normal"
+    assert {m for m, _, _, _, _ in probs("tail")} == {4000, 6144, 8200}
+    assert all(m == n == k for m, n, k, _, _ in probs("tail"))
